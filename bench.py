@@ -1,0 +1,231 @@
+#!/usr/bin/env python3
+"""Benchmark of the DSA layer hot path on one MI355X.
+
+A step is one dsa_forward (lightning indexer -> top-k -> sparse MQA-mode MLA)
+over a decode batch of 64 sequences at 131072 tokens of context, k = 2048,
+inputs (FP8 index-key cache, bf16 latent cache, queries) already resident in
+HBM.  Prints one JSON line: decode queries/s, with the indexer's roofline
+(HBM-bound; stage time from HIP events recorded on the library's stream inside
+the timed region) and the CPU oracle timed on a bounded sample of the same
+workload.  Per-stage figures and a causal-prefill measurement (16384 tokens)
+ride along under "stages" and "prefill".
+
+    python bench.py [--steps K] [--warmup W] [--no-prefill] [--no-cpu-baseline]
+"""
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA, published
+FP8_PEAK_TFLOPS = 5000.0       # dense fp8 MFMA, published
+IDX_BYTES_PER_KEY = 128 + 4 + 4  # FP8 key row + key scale read, fp32 score written
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def indexer_units(nvis, k):
+    """Keys scored in one launch (queries with n_vis <= k are bypassed)."""
+    return int(sum(int(n) for n in nvis if n > k))
+
+
+def mla_work(counts):
+    rows = int(sum(int(c) for c in counts))
+    flops = rows * 128 * (576 + 512) * 2
+    gather = rows * 1152
+    return rows, flops, gather
+
+
+def prepare(wl):
+    import sparse_long_context_dsa_amd as dsa
+    nq, rows = wl.nq, wl.rows
+    q8 = torch.empty((nq, 64, 128), dtype=torch.uint8, device="cuda")
+    qs = torch.empty((nq, 64), dtype=torch.float32, device="cuda")
+    k8 = torch.empty((rows, 128), dtype=torch.uint8, device="cuda")
+    ks = torch.empty((rows,), dtype=torch.float32, device="cuda")
+    dsa.dsa_quantize_fp8(wl.q_idx.view(nq * 64, 128), q8.view(nq * 64, 128), qs.view(nq * 64))
+    dsa.dsa_quantize_fp8(wl.k_idx, k8, ks)
+    queries = dsa.Queries(wl.q_seq, wl.q_nvis, wl.max_nvis)
+    if wl.block_size:
+        layout = dsa.KvLayout(wl.num_seqs, rows, block_table=wl.block_table, block_size=wl.block_size)
+    else:
+        layout = dsa.KvLayout(wl.num_seqs, rows, seq_row0=wl.row0)
+    out = torch.empty((nq, 128, 512), dtype=torch.float32, device="cuda")
+    lse = torch.empty((nq, 128), dtype=torch.float32, device="cuda")
+    idx = torch.empty((nq, wl.k), dtype=torch.int32, device="cuda")
+    ws = dsa.workspace(dsa.DSA_OP_FORWARD, queries, wl.k)
+    return dict(q8=q8, qs=qs, k8=k8, ks=ks, queries=queries, layout=layout, out=out, lse=lse, idx=idx, ws=ws)
+
+
+def time_forward(wl, p, steps, warmup):
+    """Returns (wall seconds for `steps` steps, per-stage mean ms)."""
+    import sparse_long_context_dsa_amd as dsa
+
+    def step(ev=None):
+        dsa.dsa_forward(p["queries"], p["layout"], p["q8"], p["qs"], wl.w, p["k8"], p["ks"], wl.q_mla, wl.kv,
+                        wl.k, wl.softmax_scale, p["out"], p["lse"], p["idx"], ws=p["ws"], events=ev)
+
+    for _ in range(warmup):
+        step()
+    ev = dsa.HipEvents(4 * steps)
+    ptr = ctypes.sizeof(ctypes.c_void_p)
+    base = ctypes.addressof(ev.handles)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step((ctypes.c_void_p * 4).from_address(base + 4 * i * ptr))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    st = {"indexer": [], "topk": [], "mla": []}
+    for i in range(steps):
+        st["indexer"].append(ev.elapsed_ms(4 * i, 4 * i + 1))
+        st["topk"].append(ev.elapsed_ms(4 * i + 1, 4 * i + 2))
+        st["mla"].append(ev.elapsed_ms(4 * i + 2, 4 * i + 3))
+    ev.close()
+    return wall, {k: float(np.mean(v)) for k, v in st.items()}
+
+
+def cpu_baseline(wl, sample, k):
+    """The oracle (NumPy float64) on the first `sample` queries of the workload.
+    Its inputs (FP8 codes from its own quantiser, bf16 rows) are prepared
+    outside the timed region, as the GPU's are."""
+    import oracle
+    from oracle.bf16 import bf16_decode  # noqa: F401  (same package, decoding happens inside the timed calls)
+    qseq = wl.q_seq.cpu().numpy()
+    nv = wl.q_nvis.cpu().numpy()
+    row0 = wl.row0.cpu().numpy() if wl.row0 is not None else None
+    bt = wl.block_table.cpu().numpy() if wl.block_table is not None else None
+    inputs = []
+    for i in range(sample):
+        rows = oracle.phys_rows(int(qseq[i]), np.arange(int(nv[i])), row0=row0, block_table=bt,
+                                block_size=wl.block_size)
+        rt = torch.from_numpy(rows).cuda()
+        q8, qs = oracle.quantize_rows(wl.q_idx[i].cpu().numpy())
+        k8, ks = oracle.quantize_rows(wl.k_idx[rt].cpu().numpy())
+        kv = wl.kv[rt].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        qm = wl.q_mla[i].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        inputs.append((q8, qs, wl.w[i].cpu().numpy(), k8, ks, qm, kv))
+        log(f"cpu baseline: prepared query {i + 1}/{sample}")
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([int(x.get("num_threads", 1)) for x in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        cores = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    for (q8, qs, w, k8, ks, qm, kv) in inputs:
+        oracle.forward_query(q8, qs, w, k8, ks, qm, kv, k, wl.softmax_scale)
+    dt = time.perf_counter() - t0
+    return {"value": sample / dt, "unit": "queries/s", "cores": cores, "kind": "oracle",
+            "sample": f"first {sample} of the 64 decode queries at 131072 context (full indexer, top-k and "
+                      f"attention per query), {dt:.1f} s"}
+
+
+def run_prefill(steps, warmup):
+    from workloads import make_config
+    log("prefill: generating 16384-token causal workload")
+    wl = make_config(3, device="cuda")
+    p = prepare(wl)
+    wall, st = time_forward(wl, p, steps, warmup)
+    nv = wl.q_nvis.cpu().numpy()
+    cnt = np.minimum(nv, wl.k)
+    pairs = indexer_units(nv, wl.k)
+    idx_flops = pairs * 64 * 128 * 2
+    rows, flops, gather = mla_work(cnt)
+    res = {
+        "workload": "prefill 16384 tokens, causal, k=2048",
+        "ms_per_step": 1e3 * wall / steps,
+        "tokens_per_s": wl.nq * steps / wall,
+        "indexer_ms": st["indexer"], "topk_ms": st["topk"], "mla_ms": st["mla"],
+        "indexer_tflops_fp8": idx_flops / (st["indexer"] * 1e-3) / 1e12,
+        "indexer_frac_fp8_peak": idx_flops / (st["indexer"] * 1e-3) / 1e12 / FP8_PEAK_TFLOPS,
+        "mla_tflops_bf16": flops / (st["mla"] * 1e-3) / 1e12,
+        "mla_frac_bf16_peak": flops / (st["mla"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+        "mla_gather_gbs": gather / (st["mla"] * 1e-3) / 1e9,
+    }
+    del wl, p
+    torch.cuda.empty_cache()
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-sample", type=int, default=6)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(decode shards by sequence with no exchange; see the design notes). "
+              f"Got --gpus {args.gpus}, WORLD_SIZE {world}.", file=sys.stderr)
+        sys.exit(2)
+
+    import sparse_long_context_dsa_amd as dsa
+    from workloads import make_config
+    dsa._lib.lib()  # fail loudly if the HIP library is missing
+    log(f"library {dsa.lib_path()}")
+    log("generating decode workload 64 x 131072 (planted keys)")
+    wl = make_config(2, device="cuda")
+    p = prepare(wl)
+    torch.cuda.synchronize()
+    log("timing dsa_forward")
+    wall, st = time_forward(wl, p, args.steps, args.warmup)
+    nv = wl.q_nvis.cpu().numpy()
+    units = indexer_units(nv, wl.k)
+    idx_bytes = units * IDX_BYTES_PER_KEY + wl.nq * (64 * 128 + 64 * 8)
+    achieved = idx_bytes / (st["indexer"] * 1e-3) / 1e9
+    topk_bytes = units * 4 + wl.nq * wl.k * 4
+    rows, flops, gather = mla_work(np.minimum(nv, wl.k))
+    mla_bytes = gather + wl.nq * (128 * 576 * 2 + 128 * 512 * 4 + wl.k * 4)
+    result = {
+        "metric": "DSA layer decode queries/s @128K ctx; indexer HBM TB/s; sparse-MLA TFLOPs",
+        "value": wl.nq * args.steps / wall,
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": 1e3 * wall / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8+bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": wl.nq, "context": int(nv.max()), "k": wl.k,
+                   "indexer_heads": 64, "indexer_dim": 128, "heads": 128, "latent": 576},
+        "roofline": {"bound": "hbm", "kernel": "indexer", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+        "stages": {
+            "indexer_ms": st["indexer"], "topk_ms": st["topk"], "mla_ms": st["mla"],
+            "indexer_gbs": achieved,
+            "topk_gbs": topk_bytes / (st["topk"] * 1e-3) / 1e9,
+            "topk_frac_hbm": topk_bytes / (st["topk"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "mla_tflops_bf16": flops / (st["mla"] * 1e-3) / 1e12,
+            "mla_gbs": mla_bytes / (st["mla"] * 1e-3) / 1e9,
+            "mla_gather_gbs": gather / (st["mla"] * 1e-3) / 1e9,
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample, wl.k)
+    del p
+    del wl
+    torch.cuda.empty_cache()
+    if not args.no_prefill:
+        result["prefill"] = run_prefill(max(2, args.steps // 4), 2)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,215 @@
+/*
+ * dsa.h - C ABI of libdsa.so, the DeepSeek Sparse Attention (DSA) hot path of
+ * one attention layer on an AMD Instinct MI355X (gfx950).
+ *
+ * The path has three stages (page "arXiv'25 | DSA ... DeepSeek-V3.2" on
+ * marsggbo.github.io, section 3, its three equations; page "DeepSeekV3.2之DSA"
+ * on yuyanqi.com, parts 3-5):
+ *   1. lightning-indexer scores I[t,s] = sum_j w[t,j] * ReLU(q[t,j] . k[s]) with
+ *      FP8 E4M3 q and k, 64 indexer heads of width 128, one key head shared by
+ *      all indexer heads;
+ *   2. per-query top-k (k <= 2048) over the visible history;
+ *   3. MQA-mode MLA attention of 128 query heads over only the selected
+ *      576-wide bf16 latent rows (512 latent dims, which are also the value, and
+ *      64 rotary dims).
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Pointers.  Every array pointer is DEVICE memory owned by the caller (for
+ *   example torch allocations).  The structs themselves are read on the host
+ *   during the call and may be freed when it returns.  The library never
+ *   allocates or frees memory: scratch space is the caller's `ws` buffer,
+ *   sized by dsa_workspace_bytes().  Arrays of 16-byte elements or rows must be
+ *   16-byte aligned; `ws` must be 256-byte aligned.
+ * Streams.  Each call enqueues its kernels on `stream` and returns at once;
+ *   nothing synchronises.  Two calls that share a workspace must be ordered
+ *   on one stream.
+ * Positions.  Query i belongs to sequence q_seq[i] and sees the positions
+ *   [0, q_nvis[i]) of that sequence (decode: the whole history of length L;
+ *   causal prefill: n_vis = t for the token at 0-based position t).  The pages
+ *   count positions from 1; the ABI counts from 0.
+ * Caches.  The index-key cache (FP8 codes k_fp8[R,128] + fp32 k_scale[R]) and
+ *   the latent cache (bf16 kv[R,576]) are stored per token and addressed by the
+ *   same positions through one dsa_kv_layout (page "DeepSeekV3.2之DSA",
+ *   part 5.2, point 3: two caches aligned by one set of indices).
+ * Errors.  Each call returns DSA_OK (0) or a status below; the arguments are
+ *   checked on the host before anything is launched, and nothing is launched
+ *   when a check fails.  Index, block-table and length VALUES in device memory
+ *   are trusted, not checked.  dsa_last_error() gives a message for the last
+ *   failing call of the calling thread.
+ */
+#ifndef LIBDSA_DSA_H_
+#define LIBDSA_DSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Compile-time shapes (page "DeepSeekV3.2之DSA", part 3.2 table and part 5.1):
+ * indexer heads and width, attention heads, latent row width, value width,
+ * and the largest supported k. */
+enum {
+  DSA_HI = 64,
+  DSA_DI = 128,
+  DSA_H = 128,
+  DSA_D = 576,
+  DSA_DV = 512,
+  DSA_KMAX = 2048
+};
+
+typedef enum dsa_status {
+  DSA_OK = 0,
+  DSA_ERR_INVALID_ARG = 1, /* null pointer, bad size, k out of [1, 2048], misalignment */
+  DSA_ERR_UNSUPPORTED = 2, /* a shape or layout this build does not handle */
+  DSA_ERR_WORKSPACE = 3,   /* ws is NULL or smaller than dsa_workspace_bytes() */
+  DSA_ERR_HIP = 4          /* a HIP launch failed */
+} dsa_status;
+
+/* Where the tokens of each sequence live in the two caches.
+ *   block_size == 0 : contiguous; position s of sequence q is row seq_row0[q] + s.
+ *   block_size  > 0 : paged; block_size is a power of two and a multiple of 64;
+ *                     position s of q is row
+ *                     block_table[q * max_blocks + s / block_size] * block_size
+ *                     + s % block_size.
+ * num_rows is R, the row count of both caches (host value, used for checks). */
+typedef struct dsa_kv_layout {
+  int32_t num_seqs;
+  int32_t block_size;
+  int32_t max_blocks;
+  int32_t reserved;
+  int64_t num_rows;
+  const int32_t *block_table; /* device int32 [num_seqs, max_blocks] if paged, else NULL */
+  const int64_t *seq_row0;    /* device int64 [num_seqs] if contiguous, else NULL */
+} dsa_kv_layout;
+
+/* The queries of one call.  max_nvis is a host-side upper bound of q_nvis[]
+ * (it sizes grids and workspaces; a smaller true maximum only wastes time). */
+typedef struct dsa_queries {
+  int32_t num_q;
+  int32_t max_nvis;
+  const int32_t *q_seq;  /* device int32 [num_q] */
+  const int32_t *q_nvis; /* device int32 [num_q], each in [0, max_nvis] */
+} dsa_queries;
+
+/* Operation ids for dsa_workspace_bytes(). */
+typedef enum dsa_op {
+  DSA_OP_TOPK = 1,
+  DSA_OP_MLA_DECODE = 2,
+  DSA_OP_MLA_PREFILL = 3,
+  DSA_OP_FORWARD = 4
+} dsa_op;
+
+/* Per-row FP8 E4M3 quantisation, the step that writes the indexer's q and
+ * key cache (page "DeepSeekV3.2之DSA", part 4.3 and part 5.2 point 3: FP8
+ * index keys with a per-key dequantisation scale).
+ *   x      : fp32 [rows, cols], row-major, 16-byte aligned;
+ *   codes  : uint8 [rows, cols] E4M3 ("fn": max 448, no infinities);
+ *   scales : fp32 [rows].
+ * scale = absmax(row) / 448 (IEEE fp32 division; 1 for an all-zero row) and
+ * code = E4M3(x / scale), rounded to nearest-even and saturated at +-448.
+ * cols must be a multiple of 64 in [64, 512]. */
+int dsa_quantize_fp8(const float *x, int64_t rows, int32_t cols, uint8_t *codes,
+                     float *scales, hipStream_t stream);
+
+/* Lightning-indexer scores (page "arXiv'25 | DSA ...", section 3, first
+ * equation; page "DeepSeekV3.2之DSA", part 4.3, operation order):
+ *   scores[i*ld + s] = k_scale[r(s)] * sum_j (w[i,j] * q_scale[i,j])
+ *                       * ReLU(sum_d q_fp8[i,j,d] * k_fp8[r(s),d])
+ * for s < q_nvis[i], where r(s) is the cache row of position s.  Entries at
+ * s >= q_nvis[i] are not written.  Any constant factor (head-count or width
+ * scaling) belongs in w.
+ *   q_fp8   : uint8 [num_q, 64, 128] E4M3;   q_scale : fp32 [num_q, 64] or NULL (= 1);
+ *   w       : fp32 [num_q, 64];
+ *   k_fp8   : uint8 [R, 128] E4M3;           k_scale : fp32 [R];
+ *   scores  : fp32 [num_q, ld], ld >= max_nvis, ld % 4 == 0. */
+int dsa_indexer_scores(const dsa_queries *queries, const dsa_kv_layout *layout,
+                       const uint8_t *q_fp8, const float *q_scale, const float *w,
+                       const uint8_t *k_fp8, const float *k_scale, float *scores,
+                       int64_t ld, hipStream_t stream);
+
+/* Top-k selection (page "arXiv'25 | DSA ...", section 3, second equation;
+ * page "DeepSeekV3.2之DSA", part 4.4: indices of the min(topk, end_pos) largest
+ * scores; part 4.5: a history no longer than k keeps every position).
+ *   scores : fp32 [num_q, ld] (only s < q_nvis[i] is read; no NaN);
+ *   idx    : int32 [num_q, k]  the count = min(k, n_vis) chosen positions in
+ *            ascending order, then -1 padding;
+ *   count  : int32 [num_q] or NULL.
+ * Ties go to the lower position; -0 and +0 compare equal.  The result is
+ * deterministic.  ws : dsa_workspace_bytes(DSA_OP_TOPK, queries, k) bytes. */
+int dsa_topk(const dsa_queries *queries, const float *scores, int64_t ld, int32_t k,
+             int32_t *idx, int32_t *count, void *ws, size_t ws_bytes,
+             hipStream_t stream);
+
+/* Sparse MQA-mode MLA attention (page "arXiv'25 | DSA ...", section 3, third
+ * equation; page "DeepSeekV3.2之DSA", part 5.1: softmax(q . [c_kv; k_pe]^T) .
+ * c_kv over the selected slots only, all 128 heads sharing one latent row).
+ *   q     : bf16 [num_q, 128, 576] (absorbed query: 512 latent + 64 rotary);
+ *   kv    : bf16 [R, 576] latent cache; the value is dims 0..511 of each row;
+ *   idx   : int32 [num_q, k] positions; the first count[i] entries are attended
+ *           (each must be < q_nvis[i]); order does not matter;
+ *   count : int32 [num_q], or NULL for min(k, q_nvis[i]);
+ *   out   : fp32 [num_q, 128, 512] = sum_r softmax_r(z) * kv[r, 0:512] with
+ *           z = softmax_scale * q . kv[r];
+ *   lse   : fp32 [num_q, 128] natural-log sum of exp(z), or NULL.
+ * An empty selection gives out = 0 and lse = -inf.
+ * _decode splits each query's rows over several workgroups and merges the
+ * partial results (for few queries); _prefill gives each query one workgroup
+ * (for many queries).  Both compute the same function.
+ * ws : dsa_workspace_bytes(DSA_OP_MLA_DECODE or _PREFILL, queries, k) bytes
+ * (0 is allowed for _prefill). */
+int dsa_sparse_mla_decode(const dsa_queries *queries, const dsa_kv_layout *layout,
+                          const uint16_t *q, const uint16_t *kv, const int32_t *idx,
+                          const int32_t *count, int32_t k, float softmax_scale,
+                          float *out, float *lse, void *ws, size_t ws_bytes,
+                          hipStream_t stream);
+int dsa_sparse_mla_prefill(const dsa_queries *queries, const dsa_kv_layout *layout,
+                           const uint16_t *q, const uint16_t *kv, const int32_t *idx,
+                           const int32_t *count, int32_t k, float softmax_scale,
+                           float *out, float *lse, void *ws, size_t ws_bytes,
+                           hipStream_t stream);
+
+/* The whole layer hot path: indexer -> top-k -> sparse attention (page
+ * "DeepSeekV3.2之DSA", part 5.1 decode data flow), with the short-history
+ * bypass of part 4.5 (a query with q_nvis <= k is not scored and attends to
+ * every visible position).  Arguments as in the stage calls above;
+ * idx_out (int32 [num_q, k]) and lse may be NULL.
+ * ws : dsa_workspace_bytes(DSA_OP_FORWARD, queries, k) bytes. */
+int dsa_forward(const dsa_queries *queries, const dsa_kv_layout *layout,
+                const uint8_t *q_fp8, const float *q_scale, const float *w,
+                const uint8_t *k_fp8, const float *k_scale, const uint16_t *q,
+                const uint16_t *kv, int32_t k, float softmax_scale, float *out,
+                float *lse, int32_t *idx_out, void *ws, size_t ws_bytes,
+                hipStream_t stream);
+
+/* dsa_forward, plus stage timing: when events is non-NULL, events[0..3]
+ * (created by the caller, NULL entries skipped) are recorded on `stream`
+ * before the indexer, between the indexer and the top-k, between the top-k
+ * and the attention, and after the attention, so that hipEventElapsedTime
+ * gives each stage's device time.  Same results as dsa_forward. */
+int dsa_forward_profiled(const dsa_queries *queries, const dsa_kv_layout *layout,
+                         const uint8_t *q_fp8, const float *q_scale, const float *w,
+                         const uint8_t *k_fp8, const float *k_scale, const uint16_t *q,
+                         const uint16_t *kv, int32_t k, float softmax_scale, float *out,
+                         float *lse, int32_t *idx_out, void *ws, size_t ws_bytes,
+                         hipStream_t stream, hipEvent_t *events);
+
+/* Workspace size in bytes for `op` with these queries and k (0 if none is
+ * needed; SIZE_MAX for invalid arguments).  Host-only, launches nothing. */
+size_t dsa_workspace_bytes(int op, const dsa_queries *queries, int32_t k);
+
+/* Static description of a status code. */
+const char *dsa_status_string(int status);
+
+/* Detail of the calling thread's last failing call ("" if none). */
+const char *dsa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBDSA_DSA_H_ */

@@ -1,0 +1,164 @@
+// Lightning-indexer scores on FP8 MFMA (gfx950).
+//
+//   I[i, s] = k_scale[r(s)] * sum_j (w[i,j] * q_scale[i,j]) * ReLU(q8[i,j,:] . k8[r(s),:])
+//
+// Page "arXiv'25 | DSA ... DeepSeek-V3.2", section 3 (first equation); page
+// "DeepSeekV3.2之DSA", part 4.3 (order: FP8 q@k into fp32, ReLU times the head
+// weight, sum over heads, times the key scale).  q_scale is folded into the
+// head weight (same page, part 4.3: the weights carry the q scale); the key
+// scale is applied after the head sum, which is exact reordering because
+// k_scale > 0 and ReLU is positively homogeneous.
+//
+// Mapping: one wavefront owns one query and a run of IDX_KPW keys.  The 64
+// indexer heads are the M side of v_mfma_scale_f32_16x16x128_f8f6f4 (4 M-tiles
+// of 16 heads, K = 128 = the whole head width, so one MFMA per 16x16 tile);
+// keys are the N side, 16 per tile, 4 tiles (64 keys) per step.  The query's
+// 8 KiB of FP8 q stays in registers for the whole run; keys stream from HBM
+// straight into the B-operand registers (each lane reads 32 contiguous bytes
+// of a key row; the two 64-byte halves of a row go to lane groups 0/1 and
+// 2/3), prefetched one step ahead.  ReLU, the weighting and 16 of the 64 head
+// terms are summed in-lane; the remaining 4-way sum across lane groups is a
+// butterfly that also transposes, so lane l ends with the score of key s0+l
+// and the 64 scores of a step leave in one coalesced 256-byte store.
+//
+// Optionally each block also builds a 2048-bin histogram of the top 11 bits
+// of the scores' order-preserving keys (the first pass of the top-k radix
+// select), so the top-k stage need not read the scores twice.
+#include "device_util.h"
+#include "dsa_internal.h"
+
+namespace dsa {
+
+constexpr int IDX_WAVES = 4;
+constexpr int IDX_KPW = 1024;                    // keys per wavefront
+constexpr int IDX_KPB = IDX_WAVES * IDX_KPW;     // keys per block
+
+__device__ __forceinline__ v4f mfma_fp8_16x16x128(const v8i &a, const v8i &b, const v4f &c) {
+  // Format 0 = FP8 E4M3 for both operands; E8M0 scale 127 = 2^0 (no scaling).
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0x7F7F7F7F, 0, 0x7F7F7F7F);
+}
+
+__device__ __forceinline__ v8i load32(const uint8_t *p) {
+  const uint4 x0 = *reinterpret_cast<const uint4 *>(p);
+  const uint4 x1 = *reinterpret_cast<const uint4 *>(p + 16);
+  v8i r;
+  r[0] = (int)x0.x; r[1] = (int)x0.y; r[2] = (int)x0.z; r[3] = (int)x0.w;
+  r[4] = (int)x1.x; r[5] = (int)x1.y; r[6] = (int)x1.z; r[7] = (int)x1.w;
+  return r;
+}
+
+struct KeyStep {
+  v8i b[4];
+  float ks;
+};
+
+// Loads the B operands (4 tiles of 16 keys) of the 64-key step at s0.
+__device__ __forceinline__ void load_step(const IndexerLaunch &a, int seq, int s0, int nvis, int lane,
+                                          KeyStep &st) {
+  const int64_t base = phys_row(a.map, seq, s0);  // 64 | block size: the step is contiguous
+  const int sub = lane & 15, half = lane >> 4;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int key = s0 + 16 * t + sub;
+    if (key < nvis) {
+      st.b[t] = load32(a.k8 + (base + 16 * t + sub) * 128 + 32 * half);
+    } else {
+      st.b[t] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+  }
+  st.ks = (s0 + lane < nvis) ? a.k_scale[base + lane] : 0.0f;
+}
+
+template <bool HIST>
+__global__ __launch_bounds__(256) void indexer_kernel(IndexerLaunch a, int nchunks) {
+  const int q = blockIdx.x / nchunks;
+  const int chunk = blockIdx.x - q * nchunks;
+  const int nvis = a.q_nvis[q];
+  if (nvis <= a.skip_le || chunk * IDX_KPB >= nvis) return;  // block-uniform
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int seq = a.q_seq[q];
+
+  __shared__ uint32_t hist[HIST ? TOPK_BINS : 1];
+  if (HIST) {
+    for (int b = threadIdx.x; b < TOPK_BINS; b += blockDim.x) hist[b] = 0u;
+    __syncthreads();
+  }
+
+  // A operands: 4 M-tiles of 16 heads; lane holds head 16*mt + (lane&15),
+  // bytes [32*(lane>>4), +32) of the 128-byte head row.
+  const uint8_t *qp = a.q8 + (int64_t)q * (64 * 128);
+  v8i A[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) A[mt] = load32(qp + (16 * mt + (lane & 15)) * 128 + 32 * (lane >> 4));
+  // Epilogue weights for the accumulator rows this lane holds:
+  // head 16*mt + 4*(lane>>4) + r.
+  float coef[4][4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int h = 16 * mt + 4 * (lane >> 4) + r;
+      const float qs = a.q_scale ? a.q_scale[(int64_t)q * 64 + h] : 1.0f;
+      coef[mt][r] = a.w[(int64_t)q * 64 + h] * qs;
+    }
+
+  const int s_begin = chunk * IDX_KPB + wave * IDX_KPW;
+  const int s_end = min(s_begin + IDX_KPW, nvis);
+  float *srow = a.scores + (int64_t)q * a.ld;
+  const int g = lane >> 4;
+  const bool b1 = (g & 2) != 0, b0 = (g & 1) != 0;
+
+  KeyStep cur, nxt;
+  if (s_begin < s_end) load_step(a, seq, s_begin, nvis, lane, cur);
+  for (int s0 = s_begin; s0 < s_end; s0 += 64) {
+    if (s0 + 64 < s_end) load_step(a, seq, s0 + 64, nvis, lane, nxt);
+    float p[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      float acc_sum = 0.0f;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const v4f c = mfma_fp8_16x16x128(A[mt], cur.b[t], v4f{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc_sum = fmaf(coef[mt][r], fmaxf(c[r], 0.0f), acc_sum);
+      }
+      p[t] = acc_sum;
+    }
+    // Reduce over the 4 lane groups and scatter: lane group g keeps tile g.
+    const float ra = shfl_xor(b1 ? p[0] : p[2], 32);
+    const float rb = shfl_xor(b1 ? p[1] : p[3], 32);
+    const float x0 = (b1 ? p[2] : p[0]) + ra;
+    const float x1 = (b1 ? p[3] : p[1]) + rb;
+    const float rc = shfl_xor(b0 ? x0 : x1, 16);
+    const float score = ((b0 ? x1 : x0) + rc) * cur.ks;
+    if (s0 + lane < s_end) {
+      srow[s0 + lane] = score;
+      if (HIST) atomicAdd(&hist[order_key(score) >> 21], 1u);
+    }
+    cur = nxt;
+  }
+
+  if (HIST) {
+    __syncthreads();
+    uint32_t *gh = a.hist + (int64_t)q * TOPK_BINS;
+    for (int b = threadIdx.x; b < TOPK_BINS; b += blockDim.x) {
+      const uint32_t c = hist[b];
+      if (c) atomicAdd(&gh[b], c);
+    }
+  }
+}
+
+hipError_t launch_indexer(const IndexerLaunch &a, hipStream_t st) {
+  if (a.num_q == 0 || a.max_nvis == 0) return hipSuccess;
+  const int nchunks = (a.max_nvis + IDX_KPB - 1) / IDX_KPB;
+  const int64_t blocks = (int64_t)a.num_q * nchunks;
+  if (a.hist)
+    hipLaunchKernelGGL(indexer_kernel<true>, dim3((unsigned)blocks), dim3(IDX_WAVES * WAVE), 0, st, a,
+                       nchunks);
+  else
+    hipLaunchKernelGGL(indexer_kernel<false>, dim3((unsigned)blocks), dim3(IDX_WAVES * WAVE), 0, st, a,
+                       nchunks);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -1,0 +1,113 @@
+"""Host-only checks of the C ABI: the library loads, exports every function
+include/dsa.h declares, sizes workspaces, and rejects bad arguments before it
+launches anything (so these run without a GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_long_context_dsa_amd as dsa
+from sparse_long_context_dsa_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "dsa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(dsa_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_is_built_and_loads():
+    assert os.path.exists(dsa.lib_path()), "run `python -m sparse_long_context_dsa_amd.build` first"
+    _lib.lib()
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert {"dsa_indexer_scores", "dsa_topk", "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill",
+            "dsa_forward", "dsa_quantize_fp8", "dsa_workspace_bytes"} <= set(names)
+    L = _lib.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(_lib.EXPORTED)
+
+
+def test_status_strings():
+    L = _lib.lib()
+    assert L.dsa_status_string(0) == b"ok"
+    assert b"workspace" in L.dsa_status_string(3)
+    assert L.dsa_status_string(99) == b"unknown status"
+
+
+def _queries(num_q, max_nvis):
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: only host-side checks run
+    return _lib.QueriesC(num_q, max_nvis, fake.value, fake.value)
+
+
+def test_workspace_sizes():
+    L = _lib.lib()
+    q = _queries(64, 131072)
+    topk = L.dsa_workspace_bytes(_lib.DSA_OP_TOPK, ctypes.byref(q), 2048)
+    assert topk >= 64 * 131072 * 8  # candidate lists
+    fwd = L.dsa_workspace_bytes(_lib.DSA_OP_FORWARD, ctypes.byref(q), 2048)
+    assert fwd >= topk + 64 * 131072 * 4  # plus the score rows
+    assert L.dsa_workspace_bytes(_lib.DSA_OP_MLA_PREFILL, ctypes.byref(q), 2048) == 0
+    dec = L.dsa_workspace_bytes(_lib.DSA_OP_MLA_DECODE, ctypes.byref(q), 2048)
+    assert dec >= 64 * 4 * 128 * 512 * 4  # four splits of fp32 partials
+    assert L.dsa_workspace_bytes(_lib.DSA_OP_TOPK, ctypes.byref(q), 0) == ctypes.c_size_t(-1).value
+    assert L.dsa_workspace_bytes(77, ctypes.byref(q), 16) == ctypes.c_size_t(-1).value
+
+
+@pytest.mark.parametrize("k", [0, -1, 2049])
+def test_topk_rejects_bad_k(k):
+    L = _lib.lib()
+    q = _queries(4, 100)
+    p = ctypes.c_void_p(0x1000)
+    st = L.dsa_topk(ctypes.byref(q), p, 128, k, p, None, p, 1 << 30, None)
+    assert st == _lib.DSA_ERR_INVALID_ARG
+    assert b"k =" in L.dsa_last_error()
+
+
+def test_topk_rejects_small_workspace_and_bad_ld():
+    L = _lib.lib()
+    q = _queries(4, 10000)
+    p = ctypes.c_void_p(0x1000)
+    assert L.dsa_topk(ctypes.byref(q), p, 10000, 2048, p, None, p, 16, None) == _lib.DSA_ERR_WORKSPACE
+    assert L.dsa_topk(ctypes.byref(q), p, 9999, 2048, p, None, p, 1 << 34, None) == _lib.DSA_ERR_INVALID_ARG
+    assert L.dsa_topk(ctypes.byref(q), p, 10002, 2048, p, None, p, 1 << 34, None) == _lib.DSA_ERR_INVALID_ARG
+
+
+def test_layout_and_alignment_checks():
+    L = _lib.lib()
+    q = _queries(2, 5000)
+    p = ctypes.c_void_p(0x1000)
+    odd = ctypes.c_void_p(0x1004)
+    bad_block = _lib.KvLayoutC(2, 48, 10, 0, 1000, p.value, None)
+    st = L.dsa_indexer_scores(ctypes.byref(q), ctypes.byref(bad_block), p, None, p, p, p, p, 5000, None)
+    assert st == _lib.DSA_ERR_UNSUPPORTED
+    no_rows = _lib.KvLayoutC(2, 0, 0, 0, 1000, None, None)
+    st = L.dsa_indexer_scores(ctypes.byref(q), ctypes.byref(no_rows), p, None, p, p, p, p, 5000, None)
+    assert st == _lib.DSA_ERR_INVALID_ARG
+    ok_layout = _lib.KvLayoutC(2, 0, 0, 0, 1000, None, p.value)
+    st = L.dsa_indexer_scores(ctypes.byref(q), ctypes.byref(ok_layout), odd, None, p, p, p, p, 5000, None)
+    assert st == _lib.DSA_ERR_INVALID_ARG
+    st = L.dsa_sparse_mla_decode(ctypes.byref(q), ctypes.byref(ok_layout), p, p, p, None, 2048, 0.07, p,
+                                 None, None, 0, None)
+    assert st == _lib.DSA_ERR_WORKSPACE
+    st = L.dsa_quantize_fp8(p, 10, 100, p, p, None)
+    assert st == _lib.DSA_ERR_UNSUPPORTED
+    st = L.dsa_forward(ctypes.byref(q), ctypes.byref(ok_layout), p, None, None, p, p, p, p, 2048, 0.07, p,
+                       None, None, p, 1 << 40, None)
+    assert st == _lib.DSA_ERR_INVALID_ARG
+
+
+def test_empty_batches_are_accepted_without_launching():
+    L = _lib.lib()
+    q = _lib.QueriesC(0, 0, None, None)
+    lay = _lib.KvLayoutC(0, 0, 0, 0, 0, None, None)
+    assert L.dsa_indexer_scores(ctypes.byref(q), ctypes.byref(lay), None, None, None, None, None, None, 0,
+                                None) == 0
+    assert L.dsa_quantize_fp8(None, 0, 128, None, None, None) == 0

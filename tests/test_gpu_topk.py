@@ -1,0 +1,101 @@
+"""GPU parity of dsa_topk: the oracle's top-k run on the same fp32 scores must
+give the same index lists bit for bit (ties to the lower position, ascending
+order, -1 padding), on the GPU's own indexer scores and on adversarial
+synthetic scores (heavy ties, signed zeros, n around k, long rows)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_long_context_dsa_amd as dsa
+from gpu_util import GpuInputs, OracleView, banner, check_topk_near_ties
+from workloads import make_config, make_custom
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_topk(scores_host, nvis, k):
+    nq = len(nvis)
+    ld = max(4, (int(max(nvis)) + 3) // 4 * 4) if nq else 4
+    s = torch.zeros((nq, ld), dtype=torch.float32)
+    for i, n in enumerate(nvis):
+        s[i, :n] = torch.from_numpy(np.asarray(scores_host[i][:n], np.float32))
+    s = s.cuda()
+    q = dsa.Queries(torch.arange(nq, dtype=torch.int32, device="cuda"),
+                    torch.tensor(nvis, dtype=torch.int32, device="cuda"), int(max(nvis)))
+    idx = torch.full((nq, k), -7, dtype=torch.int32, device="cuda")
+    cnt = torch.full((nq,), -7, dtype=torch.int32, device="cuda")
+    dsa.dsa_topk(q, s, k, idx, cnt)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), cnt.cpu().numpy()
+
+
+def assert_same(scores_host, nvis, k, where):
+    idx, cnt = gpu_topk(scores_host, nvis, k)
+    for i, n in enumerate(nvis):
+        ref, rc = oracle.topk(np.asarray(scores_host[i][:n], np.float32), k)
+        assert cnt[i] == rc, f"{where} q{i}: count {cnt[i]} vs {rc}"
+        assert (idx[i] == ref).all(), f"{where} q{i}: first mismatch at {np.argmax(idx[i] != ref)}"
+
+
+def test_gpu_scores_config0_bit_exact_and_near_ties():
+    banner("topk on config 0 scores")
+    wl = make_config(0, device="cuda")
+    g = GpuInputs(wl)
+    s = g.scores().cpu().numpy()
+    n = wl.max_nvis
+    assert_same([s[0]], [n], 2048, "config0")
+    idx, cnt = gpu_topk([s[0]], [n], 2048)
+    ref, mag = OracleView(wl).indexer(0)
+    check_topk_near_ties(idx[0], int(cnt[0]), ref, mag, 2048, "config0 vs oracle scores")
+
+
+def test_gpu_scores_ragged_paged():
+    banner("topk on ragged paged scores")
+    wl = make_custom(seq_lens=[3000, 2048, 2049, 100, 17000, 8192, 8193], device="cuda", seed=31, paged=True,
+                     plant=True)
+    g = GpuInputs(wl)
+    s = g.scores().cpu().numpy()
+    nv = wl.q_nvis.cpu().numpy().tolist()
+    assert_same(list(s), nv, 2048, "ragged")
+
+
+@pytest.mark.parametrize("k", [1, 7, 2048])
+def test_heavy_ties_and_signed_zero(k):
+    banner(f"topk ties k={k}")
+    rng = np.random.default_rng(k)
+    nvis = [0, 1, k - 1 if k > 1 else 0, k, k + 1, 5000, 40000]
+    rows = []
+    for j, n in enumerate(nvis):
+        if j % 3 == 0:
+            v = rng.integers(0, 6, n).astype(np.float32)          # integer ties
+        elif j % 3 == 1:
+            v = rng.choice(np.array([0.0, -0.0, 1.0, -1.0, 0.5], np.float32), n)
+        else:
+            v = rng.standard_normal(n).astype(np.float32)
+        rows.append(v)
+    assert_same(rows, nvis, k, f"ties k={k}")
+
+
+def test_all_equal_and_constant_rows():
+    banner("topk all equal")
+    rows = [np.full(20000, 1.5, np.float32), np.full(9000, -0.0, np.float32), np.zeros(3, np.float32)]
+    assert_same(rows, [20000, 9000, 3], 2048, "all-equal")
+
+
+def test_long_rows_131072():
+    banner("topk long rows")
+    rng = np.random.default_rng(77)
+    rows = [rng.standard_normal(131072).astype(np.float32) for _ in range(3)]
+    rows[1] = np.round(rows[1] * 4) / 4  # coarse values: many exact ties at the threshold
+    assert_same(rows, [131072, 131072, 100000], 2048, "long")
+
+
+def test_deterministic_repeat():
+    banner("topk determinism")
+    rng = np.random.default_rng(5)
+    rows = [np.round(rng.standard_normal(50000) * 8).astype(np.float32) for _ in range(4)]
+    a, ca = gpu_topk(rows, [50000] * 4, 2048)
+    b, cb = gpu_topk(rows, [50000] * 4, 2048)
+    assert (a == b).all() and (ca == cb).all()
