@@ -43,6 +43,8 @@ int check_queries(const dsa_queries *qr) {
   if (!qr) return fail(DSA_ERR_INVALID_ARG, "queries is NULL");
   if (qr->num_q < 0) return fail(DSA_ERR_INVALID_ARG, "num_q = %d < 0", qr->num_q);
   if (qr->max_nvis < 0) return fail(DSA_ERR_INVALID_ARG, "max_nvis = %d < 0", qr->max_nvis);
+  if (qr->max_nvis > dsa::MAX_NVIS)
+    return fail(DSA_ERR_UNSUPPORTED, "max_nvis = %d: histories up to %d positions", qr->max_nvis, dsa::MAX_NVIS);
   if (qr->num_q > 0 && (!qr->q_seq || !qr->q_nvis))
     return fail(DSA_ERR_INVALID_ARG, "q_seq / q_nvis must be device arrays");
   return DSA_OK;
@@ -185,9 +187,9 @@ int dsa_topk(const dsa_queries *qr, const float *scores, int64_t ld, int32_t k, 
     return fail(DSA_ERR_WORKSPACE, "workspace: need %zu bytes (256-byte aligned), got %zu", need, ws_bytes);
   dsa::TopkWs tw = dsa::topk_ws_carve(ws, qr->num_q, qr->max_nvis);
   hipError_t e = dsa::launch_topk_init(tw, qr->num_q, stream);
-  if (e == hipSuccess) e = dsa::launch_topk_hist(scores, ld, qr->q_nvis, k, tw, qr->num_q, qr->max_nvis, stream);
+  if (e == hipSuccess) e = dsa::launch_topk_hist(scores, ld, qr->q_nvis, tw, qr->num_q, qr->max_nvis, stream);
   if (e == hipSuccess)
-    e = dsa::launch_topk_select(scores, ld, qr->q_nvis, k, idx, count, tw, qr->num_q, qr->max_nvis, stream);
+    e = dsa::launch_topk_select(scores, ld, qr->q_nvis, k, idx, count, tw, qr->num_q, qr->max_nvis, false, stream);
   return hip_status(e, "top-k launch");
 }
 
@@ -238,7 +240,8 @@ static int forward_impl(const dsa_queries *qr, const dsa_kv_layout *ly, const ui
   }
   mark(1);
   if (e == hipSuccess)
-    e = dsa::launch_topk_select(fw.scores, fw.ld, qr->q_nvis, k, idx, fw.count, tw, qr->num_q, qr->max_nvis, stream);
+    e = dsa::launch_topk_select(fw.scores, fw.ld, qr->q_nvis, k, idx, fw.count, tw, qr->num_q, qr->max_nvis, true,
+                                stream);
   mark(2);
   if (e == hipSuccess) {
     dsa::MlaLaunch ma{q, kv, idx, fw.count, qr->q_seq, qr->q_nvis, m, k, qr->num_q, softmax_scale, out, lse};

@@ -44,24 +44,29 @@ struct IndexerLaunch {
 };
 hipError_t launch_indexer(const IndexerLaunch &a, hipStream_t st);
 
-// Top-k: 11-bit coarse bins of the order-preserving key, chunks of TOPK_CHUNK.
+// Top-k: radix digits of 11/11/10 bits; rows up to TOPK_ROW_MAX are selected
+// by one block from LDS, longer rows in chunks of TOPK_CHUNK.
 constexpr int TOPK_BINS = 2048;
-constexpr int TOPK_CHUNK = 8192;
+constexpr int TOPK_ROW_MAX = 16384;
+constexpr int TOPK_CHUNK = 16384;
+constexpr int TOPK_MAX_CHUNKS = 64;  // histories up to 2^20 positions
+constexpr int MAX_NVIS = TOPK_CHUNK * TOPK_MAX_CHUNKS;
 struct TopkWs {
-  uint32_t *hist;     // [num_q, TOPK_BINS]
-  uint32_t *done;     // [num_q]
+  uint32_t *hist;     // [num_q, TOPK_BINS] first-digit histogram
+  uint32_t *hist2;    // [num_q, TOPK_BINS] second-digit histogram (long rows)
+  uint32_t *done;     // [num_q] blocks finished per query (long rows)
   uint32_t *ccount;   // [num_q, nchunks]
-  uint2 *cand;        // [num_q, nchunks, TOPK_CHUNK]
-  int32_t nchunks;
+  uint2 *cand;        // [num_q, nchunks, TOPK_CHUNK] (key, position) candidates
+  int32_t nchunks;    // 0 when every row fits TOPK_ROW_MAX
 };
 size_t topk_ws_bytes(int num_q, int max_nvis);
 TopkWs topk_ws_carve(void *ws, int num_q, int max_nvis);
 hipError_t launch_topk_init(const TopkWs &ws, int num_q, hipStream_t st);
-hipError_t launch_topk_hist(const float *scores, int64_t ld, const int32_t *q_nvis, int k,
-                            const TopkWs &ws, int num_q, int max_nvis, hipStream_t st);
-hipError_t launch_topk_select(const float *scores, int64_t ld, const int32_t *q_nvis, int k,
-                              int32_t *idx, int32_t *count, const TopkWs &ws, int num_q,
-                              int max_nvis, hipStream_t st);
+hipError_t launch_topk_hist(const float *scores, int64_t ld, const int32_t *q_nvis, const TopkWs &ws, int num_q,
+                            int max_nvis, hipStream_t st);
+hipError_t launch_topk_select(const float *scores, int64_t ld, const int32_t *q_nvis, int k, int32_t *idx,
+                              int32_t *count, const TopkWs &ws, int num_q, int max_nvis, bool hist1_valid,
+                              hipStream_t st);
 
 // Sparse MLA.
 struct MlaLaunch {

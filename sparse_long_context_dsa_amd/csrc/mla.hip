@@ -11,22 +11,24 @@
 // 128 heads, so every gathered row is read from memory once and used by every
 // head.  Wavefront w owns heads [32w, 32w+32): its queries live in registers
 // for the whole run (36 x 16-byte B fragments, 144 VGPRs) and so does its
-// output accumulator O[32 heads, 512] in fp32 (16 x 32x32 tiles, 256
-// registers).  Rows arrive in tiles of 32, gathered through the position ->
-// row map into LDS, double buffered:
-//   * K layout: [32 rows][72 x 16 B] row-major (XOR-swizzled 16-byte chunks),
-//     the A operand of S^T = K . Q^T (v_mfma_f32_32x32x16_bf16, M = rows,
-//     N = heads, K = 576 in 36 steps);
-//   * V^T layout: [512 dims][32 rows] (XOR-swizzled), written by an 8x8
-//     register transpose while staging, the B operand of O = P . V (M = heads,
-//     N = dims, K = 32 rows in 2 steps).
+// output accumulator O[32 heads, 512] in fp32 (16 x 32x32 tiles in AGPRs).
+// Rows arrive in tiles of 32, gathered through the position -> row map
+// straight from global memory into LDS (global_load_lds, 16 bytes per lane,
+// no staging registers), three tiles in flight.  One row-major copy of each
+// tile serves both products:
+//   * S^T = K . Q^T (v_mfma_f32_32x32x16_bf16, M = rows, N = heads, K = 576
+//     in 36 steps): A fragments are 16-byte LDS reads of a row;
+//   * O = P . V (M = heads, N = dims, K = 32 rows in 2 steps): B fragments
+//     (4 rows of one column per lane, twice) come from the transposing LDS
+//     read ds_read_b64_tr_b16.
+// 16-byte chunks of a tile row are XOR-swizzled by the row to spread banks.
 // Computing S transposed puts each head in one lane column, so the online
 // softmax (running max m, sum l per head) needs one cross-half exchange, and
 // the S^T accumulator registers are exactly the A operand of P . V once
-// rounded to bf16 (the V^T rows are stored in the matching order).  Only the
-// per-head rescale of O needs the softmax state of other lanes; it goes
-// through a 128-byte LDS slot per wavefront and is skipped when no running max
-// changed.  exp2 with log2(e) folded into the scale.
+// rounded to bf16.  Only the per-head rescale of O needs the softmax state of
+// other lanes; it goes through a 128-byte LDS slot per wavefront, is done in
+// place on the AGPRs, and happens only when a running max grows by more than
+// 2^8 (P stays <= 256).  exp2 with log2(e) folded into the scale.
 //
 // Decode splits a query's rows over several blocks that write (O/l, lse)
 // partials; mla_combine_kernel merges them.  Prefill gives each query one
@@ -38,15 +40,20 @@ namespace dsa {
 
 constexpr int MLA_WAVES = 4;
 constexpr int MLA_THREADS = MLA_WAVES * WAVE;
-constexpr int MLA_T = 32;                          // rows per tile
-constexpr int ROW_BYTES = 576 * 2;                 // 1152
-constexpr int KL_BYTES = MLA_T * ROW_BYTES;        // 36864
-constexpr int VT_BYTES = 512 * MLA_T * 2;          // 32768
-constexpr int BUF_BYTES = KL_BYTES + VT_BYTES;     // 69632
-constexpr int MLA_MAX_ROWS = 2048;                 // rows per block (k <= 2048)
+constexpr int MLA_T = 32;                            // rows per tile
+constexpr int ROW_BYTES = 576 * 2;                   // 1152
+constexpr int TILE_BYTES = MLA_T * ROW_BYTES;        // 36864
+constexpr int NBUF = 3;                              // tiles in flight
+constexpr int LOADS_PER_WAVE = TILE_BYTES / 16 / WAVE / MLA_WAVES;  // 9
+constexpr int MLA_MAX_ROWS = 2048;                   // rows per block (k <= 2048)
+constexpr uint32_t INVALID_ROW = 0x80000000u;        // marks a position outside [0, n_vis)
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
-constexpr float RESCALE_LOG2 = 8.0f;              // lazy-rescale threshold (log2 units)
+constexpr float RESCALE_LOG2 = 8.0f;                 // lazy-rescale threshold (log2 units)
+static_assert(LOADS_PER_WAVE * 16 * WAVE * MLA_WAVES == TILE_BYTES, "tile = whole wave loads");
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 struct MlaKernelArgs {
   MlaLaunch a;
@@ -64,17 +71,10 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
-// Byte offset of 16-byte chunk `ch` (0..71) of tile row `r` in the K layout.
-__device__ __forceinline__ int kl_off(int r, int ch) { return r * ROW_BYTES + ((ch ^ ((r >> 1) & 7)) << 4); }
-// Byte offset of 16-byte row-block `rb` (0..3) of value dim `d` in the V^T layout.
-__device__ __forceinline__ int vt_off(int d, int rb) { return KL_BYTES + d * 64 + ((rb ^ ((d >> 2) & 3)) << 4); }
-
-// Tile row held in slot jj (0..7) of row-block rb (0..3) of the V^T layout.
-// Row-block rb = 2*ks2 + g collects the rows that lane group g contributes to
-// k-step ks2 of P . V: rows 16*ks2 + 4*g + {0..3} and 16*ks2 + 8 + 4*g + {0..3}.
-__device__ __forceinline__ int rb_row(int rb, int jj) {
-  return 16 * (rb >> 1) + 4 * (rb & 1) + (jj & 3) + 8 * (jj >> 2);
-}
+// Swizzle of the 16-byte chunks of tile row r (an XOR of the chunk's low bits).
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+// Byte offset of logical 16-byte chunk ch (0..71) of tile row r.
+__device__ __forceinline__ int kl_off(int r, int ch) { return r * ROW_BYTES + ((ch ^ swz(r)) << 4); }
 
 // Scales one accumulator register in place.  The accumulators live in AGPRs,
 // which VALU instructions cannot use as operands; the explicit read / multiply /
@@ -91,6 +91,25 @@ __device__ __forceinline__ void scale_acc(float &x, float s) {
       : "v"(s));
 }
 
+// S^T chain of the QK product on a VGPR accumulator.  Written as asm
+// statements so that S stays in VGPRs (next to the softmax that reads it)
+// while all 256 AGPRs hold O; register operands only, and not volatile, so
+// the LDS reads feeding them can be scheduled ahead.  Back-to-back MFMAs
+// into the same accumulator need no wait states; the drain covers the
+// MFMA-write -> VALU-read distance before the softmax reads S.
+typedef int v4i_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void mfma_s_first(v16f &acc, const uint4 &a, const uint4 &b) {
+  const v4i_t va = __builtin_bit_cast(v4i_t, a), vb = __builtin_bit_cast(v4i_t, b);
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(va), "v"(vb));
+}
+__device__ __forceinline__ void mfma_s(v16f &acc, const uint4 &a, const uint4 &b) {
+  const v4i_t va = __builtin_bit_cast(v4i_t, a), vb = __builtin_bit_cast(v4i_t, b);
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(va), "v"(vb));
+}
+__device__ __forceinline__ void mfma_s_drain(v16f &acc) {
+  asm("s_nop 7\n\ts_nop 7\n\ts_nop 3" : "+v"(acc));
+}
+
 // Values of the 16 heads whose O rows this lane holds (heads 8i + 4g + j),
 // from a 32-entry per-head array in LDS.
 __device__ __forceinline__ void read_head_values(const float *x, int g, float *v) {
@@ -104,51 +123,20 @@ __device__ __forceinline__ void read_head_values(const float *x, int g, float *v
   }
 }
 
-struct Staging {
-  uint4 v[8];  // 8 rows x dims [8*dg, 8*dg+8)
-  uint4 rope;  // one 16-byte chunk of the rotary part
-};
-
-__device__ __forceinline__ void stage_load(const uint16_t *__restrict__ kv, const int32_t *prow, int t0,
-                                           int nrows, Staging &s) {
-  const int tid = threadIdx.x;
-  const int dg = tid & 63, rb = tid >> 6;
+// Gathers tile rows [t0, t0 + 32) into buf: each lane of each wavefront moves
+// LOADS_PER_WAVE 16-byte chunks straight into LDS.  Rows past the end reuse
+// the last row (finite data, masked out of the softmax).
+__device__ __forceinline__ void issue_tile(const uint16_t *__restrict__ kv, const uint32_t *prow, int t0,
+                                           int nrows, uint8_t *buf, int wave, int lane) {
 #pragma unroll
-  for (int jj = 0; jj < 8; ++jj) {
-    const int r = t0 + rb_row(rb, jj);
-    if (r < nrows && prow[r] >= 0) {
-      s.v[jj] = *reinterpret_cast<const uint4 *>(kv + (int64_t)prow[r] * 576 + 8 * dg);
-    } else {
-      s.v[jj] = make_uint4(0u, 0u, 0u, 0u);
-    }
-  }
-  const int rr = t0 + (tid >> 3);
-  if (rr < nrows && prow[rr] >= 0) {
-    s.rope = *reinterpret_cast<const uint4 *>(kv + (int64_t)prow[rr] * 576 + 512 + 8 * (tid & 7));
-  } else {
-    s.rope = make_uint4(0u, 0u, 0u, 0u);
-  }
-}
-
-__device__ __forceinline__ void stage_store(uint8_t *buf, const Staging &s) {
-  const int tid = threadIdx.x;
-  const int dg = tid & 63, rb = tid >> 6;
-  // K layout: row-major.
-#pragma unroll
-  for (int jj = 0; jj < 8; ++jj) *reinterpret_cast<uint4 *>(buf + kl_off(rb_row(rb, jj), dg)) = s.v[jj];
-  const int rr = tid >> 3;
-  *reinterpret_cast<uint4 *>(buf + kl_off(rr, 64 + (tid & 7))) = s.rope;
-  // V^T layout: transpose the 8 rows x 8 dims block in registers.
-  const uint32_t *w = reinterpret_cast<const uint32_t *>(s.v);  // w[4*jj + dword]
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-    uint4 o;
-    o.x = __builtin_amdgcn_perm(w[4 * 1 + (e >> 1)], w[4 * 0 + (e >> 1)], sel);
-    o.y = __builtin_amdgcn_perm(w[4 * 3 + (e >> 1)], w[4 * 2 + (e >> 1)], sel);
-    o.z = __builtin_amdgcn_perm(w[4 * 5 + (e >> 1)], w[4 * 4 + (e >> 1)], sel);
-    o.w = __builtin_amdgcn_perm(w[4 * 7 + (e >> 1)], w[4 * 6 + (e >> 1)], sel);
-    *reinterpret_cast<uint4 *>(buf + vt_off(8 * dg + e, rb)) = o;
+  for (int i = 0; i < LOADS_PER_WAVE; ++i) {
+    const int slot = (wave * LOADS_PER_WAVE + i) * WAVE + lane;  // 16-byte slot of the tile
+    const int r = slot / 72, pch = slot - r * 72;
+    const int ch = pch ^ swz(r);
+    const int rr = min(t0 + r, nrows - 1);
+    const uint32_t row = prow[rr] & ~INVALID_ROW;
+    const uint16_t *src = kv + (int64_t)row * 576 + ch * 8;
+    __builtin_amdgcn_global_load_lds(src, (lds_void *)(buf + (wave * LOADS_PER_WAVE + i) * WAVE * 16), 16, 0, 0);
   }
 }
 
@@ -160,24 +148,29 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
   const int wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 5, c = lane & 31;
 
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * BUF_BYTES];
-  __shared__ __attribute__((aligned(16))) int32_t prow[MLA_MAX_ROWS + MLA_T];
+  // Three separately declared tile buffers: each has its own alias scope, so
+  // the compiler sees that reading one tile never races with the LDS DMA that
+  // fills another (one shared array would make it wait for all DMA first).
+  __shared__ __attribute__((aligned(16))) uint8_t tb0[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t tb1[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t tb2[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint32_t prow[MLA_MAX_ROWS + MLA_T];
   __shared__ __attribute__((aligned(16))) float xch[MLA_WAVES][32];
 
   const int nvis = a.q_nvis[q];
-  int cnt = a.count ? a.count[q] : min(a.k, nvis);
-  cnt = max(0, min(cnt, a.k));
+  int cnt = a.count ? a.count[q] : a.k;
+  cnt = max(0, min(cnt, min(a.k, nvis)));
   const int r0 = sp * p.rows_per_split;
   const int nrows = max(0, min(cnt, r0 + p.rows_per_split) - r0);
 
-  // Selected positions -> physical rows.
+  // Selected positions -> physical rows.  A position outside [0, n_vis) breaks
+  // the contract; it is loaded from position 0 (in bounds, finite) and masked.
   const int seq = a.q_seq[q];
   const int32_t *ip = a.idx + (int64_t)q * a.k + r0;
-  // A position outside [0, n_vis) breaks the contract; it becomes a masked
-  // zero row instead of an out-of-bounds read.
   for (int i = tid; i < nrows; i += MLA_THREADS) {
     const int pos = ip[i];
-    prow[i] = (pos >= 0 && pos < nvis) ? (int32_t)phys_row(a.map, seq, pos) : -1;
+    const bool ok = pos >= 0 && pos < nvis;
+    prow[i] = (uint32_t)phys_row(a.map, seq, ok ? pos : 0) | (ok ? 0u : INVALID_ROW);
   }
 
   // Queries of this wavefront's 32 heads: B fragments of S^T = K . Q^T.
@@ -196,30 +189,63 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
     for (int i = 0; i < 16; ++i) o[nt][i] = 0.0f;
   float m_ref = -INFINITY, l_run = 0.0f;  // per head c (both lane halves agree on m_ref)
 
+  // Per-lane LDS address bases (everything else is an immediate offset).
+  // QK: lane reads row c, logical chunk 2*ks + g; with the swizzle s = swz(c)
+  // the chunk lands at 8*(ks >> 2) + ((2*(ks & 3) + g) ^ s).
+  int qk_base[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) qk_base[j] = c * ROW_BYTES + (((2 * j + g) ^ swz(c)) << 4);
+  // PV: in each 16-lane group, lane ti points at row r = ti >> 2 of its 4-row
+  // set and at 4 columns (8 bytes) 16*th + 4*(ti & 3) + 32*nt.  The set's rows
+  // are 16*ks2 + 8*half + 4*g + r, whose swizzle is 4*half + 2*g + (r >> 1),
+  // so the XOR splits into the compile-time nt ^ half and a per-lane part.
+  const int ti = lane & 15, th = (lane >> 4) & 1;
+  const int tr_r = ti >> 2, tr_x = 2 * th + ((ti & 3) >> 1), tr_piece = ti & 1;
+  const int tr_base = (4 * g + tr_r) * ROW_BYTES + ((tr_x ^ (2 * g + (tr_r >> 1))) << 4) + (tr_piece << 3);
+
   __syncthreads();  // prow ready
   const int ntiles = (nrows + MLA_T - 1) / MLA_T;
-  Staging st;
-  if (ntiles > 0) {
-    stage_load(a.kv, prow, 0, nrows, st);
-    stage_store(smem, st);
-  }
-  __syncthreads();
+  if (ntiles > 0) issue_tile(a.kv, prow, 0, nrows, tb0, wave, lane);
+  if (ntiles > 1) issue_tile(a.kv, prow, MLA_T, nrows, tb1, wave, lane);
 
-  for (int t = 0; t < ntiles; ++t) {
+  // One tile: wait for it, start the gather of tile t + 2 into nbuf, compute.
+  auto tile_step = [&](const int t, const uint8_t *buf, uint8_t *nbuf) {
+    // Tile t must have landed (every wave's part of it): wait for this
+    // wave's loads of tile t, then the barrier.  Tile t+1 may stay in flight.
+    // A bare s_barrier: __syncthreads() would add a workgroup release fence,
+    // which waits for every outstanding LDS DMA, tile t+1 included.  LDS
+    // reads of the previous tile have completed (their MFMAs consumed them).
+    if (t + 1 < ntiles)
+      __builtin_amdgcn_s_waitcnt(0xF70 | LOADS_PER_WAVE);  // vmcnt(9)
+    else
+      __builtin_amdgcn_s_waitcnt(0xF70);                   // vmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    // The buffer of tile t-1 is free now (every wave is past its compute):
+    // start tile t + 2 into it.
+    if (t + 2 < ntiles) issue_tile(a.kv, prow, (t + 2) * MLA_T, nrows, nbuf, wave, lane);
     const int t0 = t * MLA_T;
-    if (t + 1 < ntiles) stage_load(a.kv, prow, t0 + MLA_T, nrows, st);
-    const uint8_t *buf = smem + (t & 1) * BUF_BYTES;
 
     // S^T[row, head] for 32 rows x 32 heads.
+    // K fragments are read QK_AHEAD steps ahead of their MFMA (ring buffer).
     v16f s;
+    constexpr int QK_AHEAD = 3;
+    uint4 kf[QK_AHEAD + 1];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) s[i] = 0.0f;
+    for (int ks = 0; ks < QK_AHEAD; ++ks)
+      kf[ks] = *reinterpret_cast<const uint4 *>(buf + qk_base[ks & 3] + 128 * (ks >> 2));
 #pragma unroll
     for (int ks = 0; ks < 36; ++ks) {
-      const uint4 kf = *reinterpret_cast<const uint4 *>(buf + kl_off(c, 2 * ks + g));
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(kf), as_bf(qb[ks]), s, 0, 0, 0);
-      if ((ks & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // bound the LDS reads in flight
+      if (ks + QK_AHEAD < 36)
+        kf[(ks + QK_AHEAD) % (QK_AHEAD + 1)] =
+            *reinterpret_cast<const uint4 *>(buf + qk_base[(ks + QK_AHEAD) & 3] + 128 * ((ks + QK_AHEAD) >> 2));
+      if (ks == 0)
+        mfma_s_first(s, kf[0], qb[0]);
+      else
+        mfma_s(s, kf[ks % (QK_AHEAD + 1)], qb[ks]);
     }
+    mfma_s_drain(s);
 
     // Online softmax for head c over this tile's rows 8i + 4g + j.
     float z[16];
@@ -227,24 +253,23 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int rbase = t0 + 8 * i + 4 * g;
-      const int4 pr = *reinterpret_cast<const int4 *>(&prow[rbase]);
-      const int prv[4] = {pr.x, pr.y, pr.z, pr.w};
+      const uint4 pr = *reinterpret_cast<const uint4 *>(&prow[rbase]);
+      const uint32_t prv[4] = {pr.x, pr.y, pr.z, pr.w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int row = rbase + j;
-        const float v = (row < nrows && prv[j] >= 0) ? s[4 * i + j] * p.scale_log2 : -INFINITY;
+        const bool ok = (rbase + j < nrows) && !(prv[j] & INVALID_ROW);
+        const float v = ok ? s[4 * i + j] * p.scale_log2 : -INFINITY;
         z[4 * i + j] = v;
         tmax = fmaxf(tmax, v);
       }
     }
     tmax = fmaxf(tmax, shfl_xor(tmax, 32));
     // The reference max moves only when a head's tile max exceeds it by more
-    // than RESCALE_LOG2 (always on the first tile), so P <= 2^RESCALE_LOG2 and
-    // O is rescaled rarely.
-    // A tile whose rows are all masked leaves tmax = -inf and changes nothing.
+    // than RESCALE_LOG2 (always on the first tile with a valid row), so P <=
+    // 2^RESCALE_LOG2 and O is rescaled rarely.  An all-masked tile changes nothing.
     if (__ballot(tmax > m_ref + RESCALE_LOG2) != 0ull) {
       const float m_new = fmaxf(m_ref, tmax);
-      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);  // 0 on the first tile
+      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);  // 0 while m_ref = -inf
       l_run *= alpha;
       m_ref = m_new;
       if (t > 0) {  // O is still zero on the first tile
@@ -277,20 +302,41 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
     }
     l_run += psum;
 
-    // O += P . V over the tile's 32 rows (2 k-steps of 16).
+    // O += P . V over the tile's 32 rows (2 k-steps of 16).  The k-slots of
+    // lane group g in step ks2 are rows 16*ks2 + 4g + {0..3} and
+    // 16*ks2 + 8 + 4g + {0..3} (where the S^T accumulator put them); the
+    // transposing read gives lane l the 4 rows of one of those sets at column
+    // n = l % 32: lanes 4r..4r+3 of each 16-lane group point at row r of the
+    // set, 4 columns each.
+    // 32 steps j = (ks2, nt); the B fragment of step j is read PV_AHEAD steps
+    // ahead of its MFMA (ring buffer).
+    constexpr int PV_AHEAD = 2;
+    auto v_frag = [&](int j) {
+      const int ks2 = j >> 4, nt = j & 15;
+      const int off0 = tr_base + (16 * ks2) * ROW_BYTES + 64 * nt;            // half 0
+      const int off1 = tr_base + (16 * ks2 + 8) * ROW_BYTES + 64 * (nt ^ 1);  // half 1
+      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)(buf + off0));
+      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)(buf + off1));
+      const uint2 ulo = __builtin_bit_cast(uint2, lo), uhi = __builtin_bit_cast(uint2, hi);
+      return make_uint4(ulo.x, ulo.y, uhi.x, uhi.y);
+    };
+    uint4 vf[PV_AHEAD + 1];
 #pragma unroll
-    for (int ks2 = 0; ks2 < 2; ++ks2) {
-      const uint4 pa = make_uint4(pk[4 * ks2 + 0], pk[4 * ks2 + 1], pk[4 * ks2 + 2], pk[4 * ks2 + 3]);
+    for (int j = 0; j < PV_AHEAD; ++j) vf[j] = v_frag(j);
+    const uint4 pa0 = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    const uint4 pa1 = make_uint4(pk[4], pk[5], pk[6], pk[7]);
 #pragma unroll
-      for (int nt = 0; nt < 16; ++nt) {
-        const uint4 vf = *reinterpret_cast<const uint4 *>(buf + vt_off(32 * nt + c, 2 * ks2 + g));
-        o[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(pa), as_bf(vf), o[nt], 0, 0, 0);
-        if ((nt & 3) == 3) __builtin_amdgcn_sched_barrier(0);
-      }
+    for (int j = 0; j < 32; ++j) {
+      if (j + PV_AHEAD < 32) vf[(j + PV_AHEAD) % (PV_AHEAD + 1)] = v_frag(j + PV_AHEAD);
+      const int nt = j & 15;
+      o[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(j < 16 ? pa0 : pa1), as_bf(vf[j % (PV_AHEAD + 1)]),
+                                                      o[nt], 0, 0, 0);
     }
-
-    if (t + 1 < ntiles) stage_store(smem + ((t + 1) & 1) * BUF_BYTES, st);
-    __syncthreads();
+  };
+  for (int t = 0; t < ntiles; t += NBUF) {
+    tile_step(t, tb0, tb2);
+    if (t + 1 < ntiles) tile_step(t + 1, tb1, tb0);
+    if (t + 2 < ntiles) tile_step(t + 2, tb2, tb1);
   }
 
   // Normalise.  Both lane halves hold partial sums of head c.
