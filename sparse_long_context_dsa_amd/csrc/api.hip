@@ -7,7 +7,7 @@
 #include <cstring>
 #include <string>
 
-#include "../../include/dsa.h"
+#include "dsa.h"
 #include "dsa_internal.h"
 
 namespace {

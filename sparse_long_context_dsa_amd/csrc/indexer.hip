@@ -18,8 +18,9 @@
 // of a key row; the two 64-byte halves of a row go to lane groups 0/1 and
 // 2/3), prefetched one step ahead.  ReLU, the weighting and 16 of the 64 head
 // terms are summed in-lane; the remaining 4-way sum across lane groups is a
-// butterfly that also transposes, so lane l ends with the score of key s0+l
-// and the 64 scores of a step leave in one coalesced 256-byte store.
+// butterfly that also transposes, so lane l ends with the score of key s0+l.
+// Scores of four steps are staged in LDS and leave as 16-byte stores (1 KiB
+// per wavefront instruction).
 //
 // Optionally each block also builds a 2048-bin histogram of the top 11 bits
 // of the scores' order-preserving keys (the first pass of the top-k radix
@@ -30,7 +31,7 @@
 namespace dsa {
 
 constexpr int IDX_WAVES = 4;
-constexpr int IDX_KPW = 1024;                    // keys per wavefront
+constexpr int IDX_KPW = 512;                     // keys per wavefront (multiple of 256)
 constexpr int IDX_KPB = IDX_WAVES * IDX_KPW;     // keys per block
 
 __device__ __forceinline__ v4f mfma_fp8_16x16x128(const v8i &a, const v8i &b, const v4f &c) {
@@ -79,6 +80,10 @@ __global__ __launch_bounds__(256) void indexer_kernel(IndexerLaunch a, int nchun
   const int seq = a.q_seq[q];
 
   __shared__ uint32_t hist[HIST ? TOPK_BINS : 1];
+  // Per-wavefront staging of 256 scores: written as 16-byte stores (1 KiB per
+  // wavefront instruction), which the memory system takes much better than
+  // one 256-byte store per 64 keys.
+  __shared__ __attribute__((aligned(16))) float sbuf[IDX_WAVES][256];
   if (HIST) {
     for (int b = threadIdx.x; b < TOPK_BINS; b += blockDim.x) hist[b] = 0u;
     __syncthreads();
@@ -131,9 +136,27 @@ __global__ __launch_bounds__(256) void indexer_kernel(IndexerLaunch a, int nchun
     const float x1 = (b1 ? p[3] : p[1]) + rb;
     const float rc = shfl_xor(b0 ? x0 : x1, 16);
     const float score = ((b0 ? x1 : x0) + rc) * cur.ks;
-    if (s0 + lane < s_end) {
-      srow[s0 + lane] = score;
-      if (HIST) atomicAdd(&hist[order_key(score) >> 21], 1u);
+    const int j = ((s0 - s_begin) >> 6) & 3;  // step within the 256-key group
+    sbuf[wave][64 * j + lane] = score;
+    if (j == 3 || s0 + 64 >= s_end) {
+      // Flush the group: lane l writes keys g0 + 4l .. g0 + 4l + 3.
+      const int g0 = s0 - 64 * j;
+      const float4 v = *reinterpret_cast<const float4 *>(&sbuf[wave][4 * lane]);
+      const int p0 = g0 + 4 * lane;
+      if (p0 + 3 < s_end) {
+        *reinterpret_cast<float4 *>(srow + p0) = v;
+      } else {
+        const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (p0 + e < s_end) srow[p0 + e] = vv[e];
+      }
+      if (HIST) {
+        const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (p0 + e < s_end) atomicAdd(&hist[order_key(vv[e]) >> 21], 1u);
+      }
     }
     cur = nxt;
   }
