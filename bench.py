@@ -10,11 +10,18 @@ the timed region) and the CPU oracle timed on a bounded sample of the same
 workload.  Per-stage figures and a causal-prefill measurement (16384 tokens)
 ride along under "stages" and "prefill".
 
-    python bench.py [--steps K] [--warmup W] [--no-prefill] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload decode|prefill]
+                    [--no-prefill] [--no-cpu-baseline] [--cpu-sample N] [--copy-calib]
+
+--workload prefill makes the 16384-token causal prefill the measured workload
+(used to profile it on its own).  --copy-calib runs, after the timed steps, a
+plain 1 GiB device-to-device elementwise copy whose HBM counter readings give
+the scale for the counter-based traffic figure.
 """
 
 import argparse
 import ctypes
+import hashlib
 import json
 import os
 import sys
@@ -27,10 +34,40 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA, published
 FP8_PEAK_TFLOPS = 5000.0       # dense fp8 MFMA, published
 IDX_BYTES_PER_KEY = 128 + 4 + 4  # FP8 key row + key scale read, fp32 score written
+CALIB_BYTES = 1 << 30           # size of the calibration copy (read and written)
+
+# HBM traffic of one indexer launch on the decode workload, from two rocprofv3
+# --pmc runs (FETCH_SIZE, WRITE_SIZE; KiB per dispatch), each scaled by what the
+# same counter reads for the 1 GiB calibration copy.  Valid only for the kernel
+# source it was measured on: the figure is dropped when indexer.hip changes.
+INDEXER_TRAFFIC = {
+    "source_sha": "3396ec7e97c6d667",
+    "fetch_kib": 542919, "write_kib": 34464,          # raw counter readings
+    "calib_fetch_kib": 524294, "calib_write_kib": 1048576,  # the 1 GiB copy
+    "bytes_per_launch": 1147176523,
+}
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_sha(name):
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "sparse_long_context_dsa_amd", "csrc", name)
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def calibration_copy(reps=3):
+    """A plain elementwise copy of CALIB_BYTES, for scaling HBM counters."""
+    n = CALIB_BYTES // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def indexer_units(nvis, k):
@@ -134,6 +171,8 @@ def run_prefill(steps, warmup):
     log("prefill: generating 16384-token causal workload")
     wl = make_config(3, device="cuda")
     p = prepare(wl)
+    torch.cuda.synchronize()
+    log("prefill: timing dsa_forward")
     wall, st = time_forward(wl, p, steps, warmup)
     nv = wl.q_nvis.cpu().numpy()
     cnt = np.minimum(nv, wl.k)
@@ -156,36 +195,46 @@ def run_prefill(steps, warmup):
     return res
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cpu-sample", type=int, default=6)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-prefill", action="store_true")
-    args = ap.parse_args()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(decode shards by sequence with no exchange; see the design notes). "
-              f"Got --gpus {args.gpus}, WORLD_SIZE {world}.", file=sys.stderr)
-        sys.exit(2)
+def common_fields(args):
+    return {"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "fp8+bf16", "data": "synthetic"}
 
-    import sparse_long_context_dsa_amd as dsa
+
+def prefill_result(args):
+    pf = run_prefill(args.steps, args.warmup)
+    mla_achieved = pf["mla_tflops_bf16"]
+    result = {"metric": "DSA layer prefill tokens/s (16384-token causal sequence)",
+              "value": pf["tokens_per_s"], "unit": "tokens/s"}
+    result.update(common_fields(args))
+    result.update({
+        "ms_per_step": pf["ms_per_step"],
+        "config": {"workload": pf["workload"], "tokens": 16384, "k": 2048, "indexer_heads": 64,
+                   "indexer_dim": 128, "heads": 128, "latent": 576},
+        "roofline": {"bound": "mfma", "kernel": "sparse_mla", "achieved": mla_achieved,
+                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": mla_achieved / BF16_PEAK_TFLOPS,
+                     "traffic": None},
+        "stages": pf,
+    })
+    return result
+
+
+def decode_result(args):
+    import sparse_long_context_dsa_amd as dsa  # noqa: F401
     from workloads import make_config
-    dsa._lib.lib()  # fail loudly if the HIP library is missing
-    log(f"library {dsa.lib_path()}")
     log("generating decode workload 64 x 131072 (planted keys)")
     wl = make_config(2, device="cuda")
     p = prepare(wl)
     torch.cuda.synchronize()
     log("timing dsa_forward")
     wall, st = time_forward(wl, p, args.steps, args.warmup)
+    log("timed region done")
     nv = wl.q_nvis.cpu().numpy()
     units = indexer_units(nv, wl.k)
     idx_bytes = units * IDX_BYTES_PER_KEY + wl.nq * (64 * 128 + 64 * 8)
     achieved = idx_bytes / (st["indexer"] * 1e-3) / 1e9
+    traffic = None
+    if INDEXER_TRAFFIC is not None and INDEXER_TRAFFIC["source_sha"] == source_sha("indexer.hip"):
+        traffic = INDEXER_TRAFFIC["bytes_per_launch"] / (st["indexer"] * 1e-3) / 1e9
     topk_bytes = units * 4 + wl.nq * wl.k * 4
     rows, flops, gather = mla_work(np.minimum(nv, wl.k))
     mla_bytes = gather + wl.nq * (128 * 576 * 2 + 128 * 512 * 4 + wl.k * 4)
@@ -193,19 +242,15 @@ def main():
         "metric": "DSA layer decode queries/s @128K ctx; indexer HBM TB/s; sparse-MLA TFLOPs",
         "value": wl.nq * args.steps / wall,
         "unit": "queries/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+    }
+    result.update(common_fields(args))
+    result.update({
         "ms_per_step": 1e3 * wall / args.steps,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "fp8+bf16",
-        "data": "synthetic",
         "config": {"workload": wl.name, "batch": wl.nq, "context": int(nv.max()), "k": wl.k,
                    "indexer_heads": 64, "indexer_dim": 128, "heads": 128, "latent": 576},
         "roofline": {"bound": "hbm", "kernel": "indexer", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None},
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": idx_bytes},
         "stages": {
             "indexer_ms": st["indexer"], "topk_ms": st["topk"], "mla_ms": st["mla"],
             "indexer_gbs": achieved,
@@ -215,7 +260,12 @@ def main():
             "mla_gbs": mla_bytes / (st["mla"] * 1e-3) / 1e9,
             "mla_gather_gbs": gather / (st["mla"] * 1e-3) / 1e9,
         },
-    }
+    })
+    if traffic is not None:
+        result["roofline"]["traffic_bytes_per_launch"] = INDEXER_TRAFFIC["bytes_per_launch"]
+    if args.copy_calib:
+        log("calibration copy")
+        calibration_copy()
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample, wl.k)
@@ -224,6 +274,37 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_prefill:
         result["prefill"] = run_prefill(max(2, args.steps // 4), 2)
+    return result
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", choices=("decode", "prefill"), default="decode")
+    ap.add_argument("--cpu-sample", type=int, default=16)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--copy-calib", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(decode shards by sequence with no exchange; see the design notes). "
+              f"Got --gpus {args.gpus}, WORLD_SIZE {world}.", file=sys.stderr)
+        sys.exit(2)
+
+    import sparse_long_context_dsa_amd as dsa
+    dsa._lib.lib()  # fail loudly if the HIP library is missing
+    log(f"library {dsa.lib_path()}")
+    if args.workload == "prefill":
+        result = prefill_result(args)
+        if args.copy_calib:
+            log("calibration copy")
+            calibration_copy()
+    else:
+        result = decode_result(args)
     print(json.dumps(result), flush=True)
 
 
