@@ -7,52 +7,13 @@
 * short histories (n_vis <= k) attend to everything;
 * two runs are bit-identical."""
 
-import numpy as np
 import pytest
 import torch
 
-import oracle
-import sparse_long_context_dsa_amd as dsa
-from gpu_util import GpuInputs, OracleView, banner, check_out, check_topk_near_ties
+from gpu_util import GpuInputs, banner, check_queries, run_forward
 from workloads import make_config, make_custom
 
 pytestmark = pytest.mark.gpu
-
-
-def run_forward(g, k=None):
-    wl = g.wl
-    k = k or wl.k
-    out = torch.full((wl.nq, 128, 512), float("nan"), dtype=torch.float32, device="cuda")
-    lse = torch.full((wl.nq, 128), float("nan"), dtype=torch.float32, device="cuda")
-    idx = torch.full((wl.nq, k), -7, dtype=torch.int32, device="cuda")
-    dsa.dsa_forward(g.queries, g.layout, g.q8, g.qs, wl.w, g.k8, g.ks, wl.q_mla, wl.kv, k, wl.softmax_scale,
-                    out, lse, idx)
-    torch.cuda.synchronize()
-    return out, lse, idx
-
-
-def check_queries(wl, g, out, lse, idx, queries, k=None, near_ties=True):
-    k = k or wl.k
-    ov = OracleView(wl)
-    nv = wl.q_nvis.cpu().numpy()
-    need_scores = any(int(nv[i]) > k for i in queries)
-    s = g.scores().cpu().numpy() if need_scores else None
-    idx_h, out_h, lse_h = idx.cpu().numpy(), out.cpu().numpy(), lse.cpu().numpy()
-    for i in queries:
-        n = int(nv[i])
-        if n <= k:
-            want = np.full(k, -1)
-            want[:n] = np.arange(n)
-            assert (idx_h[i] == want).all(), f"q{i}: short history must select everything"
-            count = n
-        else:
-            ref_idx, count = oracle.topk(s[i, :n], k)
-            assert (idx_h[i] == ref_idx).all(), f"q{i}: selection differs from the oracle top-k of GPU scores"
-            if near_ties:
-                ref_scores, mag = ov.indexer(i)
-                check_topk_near_ties(idx_h[i], count, ref_scores, mag, k, f"q{i}")
-        o_ref, l_ref = ov.mla(i, idx_h[i, :count])
-        check_out(out_h[i], o_ref, lse_h[i], l_ref, f"{wl.name} q{i}")
 
 
 def test_config0():
