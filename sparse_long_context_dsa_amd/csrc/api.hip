@@ -133,7 +133,8 @@ int mla_common(bool decode, const dsa_queries *qr, const dsa_kv_layout *ly, cons
   const size_t need = dsa::mla_ws_bytes(qr->num_q, k, decode);
   if (need > 0 && (!ws || ws_bytes < need || !aligned(ws, 256)))
     return fail(DSA_ERR_WORKSPACE, "workspace: need %zu bytes (256-byte aligned), got %zu", need, ws_bytes);
-  dsa::MlaLaunch a{q, kv, idx, count, qr->q_seq, qr->q_nvis, m, k, qr->num_q, softmax_scale, out, lse};
+  dsa::MlaLaunch a{q, kv, idx, count, qr->q_seq, qr->q_nvis, m, k, qr->num_q, softmax_scale, out, lse,
+                   ly->num_rows};
   return hip_status(dsa::launch_mla(a, decode, ws, stream), "sparse MLA launch");
 }
 
@@ -244,7 +245,8 @@ static int forward_impl(const dsa_queries *qr, const dsa_kv_layout *ly, const ui
                                 stream);
   mark(2);
   if (e == hipSuccess) {
-    dsa::MlaLaunch ma{q, kv, idx, fw.count, qr->q_seq, qr->q_nvis, m, k, qr->num_q, softmax_scale, out, lse};
+    dsa::MlaLaunch ma{q, kv, idx, fw.count, qr->q_seq, qr->q_nvis, m, k, qr->num_q, softmax_scale, out, lse,
+                    ly->num_rows};
     const bool decode = dsa::mla_num_splits(qr->num_q, k, true) > 1;
     e = dsa::launch_mla(ma, decode, fw.mla, stream);
   }

@@ -82,6 +82,7 @@ struct MlaLaunch {
   float softmax_scale;
   float *out;
   float *lse;            // may be null
+  int64_t num_rows;      // rows of the latent cache
 };
 int mla_num_splits(int num_q, int k, bool decode);
 size_t mla_ws_bytes(int num_q, int k, bool decode);

@@ -66,15 +66,24 @@ struct MlaKernelArgs {
 
 __device__ __forceinline__ v8bf as_bf(const uint4 &u) { return __builtin_bit_cast(v8bf, u); }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+// Two floats -> two bf16 (round to nearest even) in one word, lo in the low half.
 __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  const __bf16 a = (__bf16)lo, b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
-// Swizzle of the 16-byte chunks of tile row r (an XOR of the chunk's low bits).
-__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
-// Byte offset of logical 16-byte chunk ch (0..71) of tile row r.
-__device__ __forceinline__ int kl_off(int r, int ch) { return r * ROW_BYTES + ((ch ^ swz(r)) << 4); }
+// Tile layout in LDS.  The 32 rows x 72 chunks (16 bytes) of a tile are
+// stored in four 9216-byte groups of 8 rows; inside a group, chunk block
+// c >> 3 (9 blocks of 1 KiB) holds the 8 rows x 8 chunks as [row & 7][slot],
+// slot = (c & 7) ^ (r & 7) ^ ((r >> 3) & 1).  A gather instruction then fills
+// one contiguous 1 KiB block (lane l: row l >> 3, slot l & 7) and each lane
+// reads a single cache row per tile; the XOR spreads the 16 rows that one
+// 16-byte read instruction serves per cycle over all 16 bank groups.
+__device__ __forceinline__ int tile_off(int r, int c) {
+  return 9216 * (r >> 3) + 1024 * (c >> 3) + 128 * (r & 7) + 16 * ((c & 7) ^ (r & 7) ^ ((r >> 3) & 1));
+}
 
 // Scales one accumulator register in place.  The accumulators live in AGPRs,
 // which VALU instructions cannot use as operands; the explicit read / multiply /
@@ -123,30 +132,72 @@ __device__ __forceinline__ void read_head_values(const float *x, int g, float *v
   }
 }
 
-// Gathers tile rows [t0, t0 + 32) into buf: each lane of each wavefront moves
-// LOADS_PER_WAVE 16-byte chunks straight into LDS.  Rows past the end reuse
-// the last row (finite data, masked out of the softmax).
-__device__ __forceinline__ void issue_tile(const uint16_t *__restrict__ kv, const uint32_t *prow, int t0,
-                                           int nrows, uint8_t *buf, int wave, int lane) {
+// Gathers this wavefront's share of the tile whose first row is prow entry r0:
+// tile rows 8*wave .. 8*wave+7, lane l taking row l >> 3 and, in part i,
+// chunk 8*i + ((l & 7) ^ (l >> 3) ^ (wave & 1)), into 1 KiB block i of the
+// wavefront's 8-row group (see tile_off).  When `real` is false the parts
+// read the block's first row into the (free) buffer instead, so the caller's
+// instruction stream has no branch.
+//
+// The load is the buffer form (MUBUF) with one descriptor per block whose
+// base is row `brow` of the cache, so every offset fits in 32 bits: a
+// contiguous cache keeps a block's rows inside one sequence (< 2^20 rows), a
+// paged pool below 4 GiB starts at row 0.  The compiler tracks this form as a
+// plain memory load, so LDS reads issued while it is in flight keep exact wait
+// counts.  A paged pool of 4 GiB or more (WIDE) takes the global form with
+// 64-bit per-lane addresses, which the compiler treats as touching LDS and
+// memory both: its LDS reads then wait for all LDS traffic.
+template <bool WIDE>
+__device__ __forceinline__ void issue_tile(const __amdgpu_buffer_rsrc_t rs, const uint16_t *__restrict__ kv,
+                                           uint32_t brow, const uint32_t *prow, int r0, bool real, uint8_t *buf,
+                                           int wave, int lane) {
+  const int rl = lane >> 3;
+  const uint32_t row = prow[real ? r0 + 8 * wave + rl : 0] & ~INVALID_ROW;
+  const int cx = (lane & 7) ^ rl ^ (wave & 1);
+  uint8_t *dst = buf + 9216 * wave;
+  if (WIDE) {
+    const uint16_t *src = kv + (size_t)row * 576 + 8 * cx;
 #pragma unroll
-  for (int i = 0; i < LOADS_PER_WAVE; ++i) {
-    const int slot = (wave * LOADS_PER_WAVE + i) * WAVE + lane;  // 16-byte slot of the tile
-    const int r = slot / 72, pch = slot - r * 72;
-    const int ch = pch ^ swz(r);
-    const int rr = min(t0 + r, nrows - 1);
-    const uint32_t row = prow[rr] & ~INVALID_ROW;
-    const uint16_t *src = kv + (int64_t)row * 576 + ch * 8;
-    __builtin_amdgcn_global_load_lds(src, (lds_void *)(buf + (wave * LOADS_PER_WAVE + i) * WAVE * 16), 16, 0, 0);
+    for (int i = 0; i < LOADS_PER_WAVE; ++i)
+      __builtin_amdgcn_global_load_lds(src + 64 * i, (lds_void *)(dst + 1024 * i), 16, 0, 0);
+  } else {
+    const uint32_t voff = (row - brow) * ROW_BYTES + 16 * cx;
+#pragma unroll
+    for (int i = 0; i < LOADS_PER_WAVE; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(dst + 1024 * i), 16, voff + 128 * i, 0, 0, 0);
   }
 }
 
+// max(a, b, c) in one instruction.  fmaxf would add a canonicalising
+// instruction per operand for values the compiler cannot see (accumulators
+// written by inline asm); the scores are never signalling NaNs.
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// Maximum / sum of v over lanes l and l ^ 32 (one cross-half swap).
+__device__ __forceinline__ float xhalf_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+  return max3f(a, b, b);
+}
+__device__ __forceinline__ float xhalf_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <bool WIDE>
 __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
   const MlaLaunch &a = p.a;
   const int q = blockIdx.x / p.nsplit;
   const int sp = blockIdx.x - q * p.nsplit;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave-uniform
   const int g = lane >> 5, c = lane & 31;
+  const int dh = wave & 1;        // half of the value dims this wavefront accumulates
+  const int partner = wave ^ 1;   // the wavefront owning the other 32 heads of the pair
 
   // Three separately declared tile buffers: each has its own alias scope, so
   // the compiler sees that reading one tile never races with the LDS DMA that
@@ -155,7 +206,14 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t tb1[TILE_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t tb2[TILE_BYTES];
   __shared__ __attribute__((aligned(16))) uint32_t prow[MLA_MAX_ROWS + MLA_T];
-  __shared__ __attribute__((aligned(16))) float xch[MLA_WAVES][32];
+  // Per-tile exchange within a wavefront pair: P of the sender's 32 heads as
+  // bf16 A fragments (lane-major, 2 x 16 bytes per lane), the rescale flag
+  // and factors.  One slot per wavefront suffices: the partner's reads of
+  // tile t complete (their MFMAs consume them) before it reaches the barrier
+  // that precedes the sender's writes of tile t + 1.
+  __shared__ __attribute__((aligned(16))) uint4 pex[MLA_WAVES][2][WAVE];
+  __shared__ __attribute__((aligned(16))) float aex[MLA_WAVES][32];
+  __shared__ int fex[MLA_WAVES];
 
   const int nvis = a.q_nvis[q];
   int cnt = a.count ? a.count[q] : a.k;
@@ -167,13 +225,23 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
   // the contract; it is loaded from position 0 (in bounds, finite) and masked.
   const int seq = a.q_seq[q];
   const int32_t *ip = a.idx + (int64_t)q * a.k + r0;
+  int bad = 0;
   for (int i = tid; i < nrows; i += MLA_THREADS) {
     const int pos = ip[i];
     const bool ok = pos >= 0 && pos < nvis;
     prow[i] = (uint32_t)phys_row(a.map, seq, ok ? pos : 0) | (ok ? 0u : INVALID_ROW);
+    bad |= ok ? 0 : 1;
+  }
+  // The rest of the last tile repeats the last row (finite data, masked out of
+  // the softmax), so the gathers need no clamping.
+  const int nrows_pad = (nrows + MLA_T - 1) / MLA_T * MLA_T;
+  if (nrows > 0 && tid < nrows_pad - nrows) {
+    const int pos = ip[nrows - 1];
+    const bool ok = pos >= 0 && pos < nvis;
+    prow[nrows + tid] = (uint32_t)phys_row(a.map, seq, ok ? pos : 0) | (ok ? 0u : INVALID_ROW);
   }
 
-  // Queries of this wavefront's 32 heads: B fragments of S^T = K . Q^T.
+  // Queries of this wavefront's own 32 heads: B fragments of S^T = K . Q^T.
   const int head = 32 * wave + c;
   uint4 qb[36];
   {
@@ -182,31 +250,48 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
     for (int ks = 0; ks < 36; ++ks) qb[ks] = *reinterpret_cast<const uint4 *>(qr + 16 * ks);
   }
 
-  v16f o[16];
+  // O[mt][nt]: M-tile 0 = own heads, 1 = partner heads; N-tile nt = value
+  // dims 256*dh + 32*nt .. +31.
+  v16f o[2][8];
 #pragma unroll
-  for (int nt = 0; nt < 16; ++nt)
+  for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) o[nt][i] = 0.0f;
-  float m_ref = -INFINITY, l_run = 0.0f;  // per head c (both lane halves agree on m_ref)
+    for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[mt][nt][i] = 0.0f;
+  float m_ref = -INFINITY, l_run = 0.0f;  // per own head c (both lane halves agree on m_ref)
 
   // Per-lane LDS address bases (everything else is an immediate offset).
-  // QK: lane reads row c, logical chunk 2*ks + g; with the swizzle s = swz(c)
-  // the chunk lands at 8*(ks >> 2) + ((2*(ks & 3) + g) ^ s).
+  // QK: lane reads row c, chunk 2*ks + g = tile_off(c, 2*ks + g)
+  // = qk_base[ks & 3] + 1024 * (ks >> 2).
   int qk_base[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) qk_base[j] = c * ROW_BYTES + (((2 * j + g) ^ swz(c)) << 4);
+  for (int j = 0; j < 4; ++j) qk_base[j] = tile_off(c, 2 * j + g);
   // PV: in each 16-lane group, lane ti points at row r = ti >> 2 of its 4-row
-  // set and at 4 columns (8 bytes) 16*th + 4*(ti & 3) + 32*nt.  The set's rows
-  // are 16*ks2 + 8*half + 4*g + r, whose swizzle is 4*half + 2*g + (r >> 1),
-  // so the XOR splits into the compile-time nt ^ half and a per-lane part.
+  // set and at 4 columns (8 bytes, piece ti & 1 of chunk 4*nt + tr_x) of
+  // this wavefront's value half.  The set's rows are 16*ks2 + 8*half + 4*g +
+  // r: row group 2*ks2 + half, row 4*g + r inside it, so tile_off splits into
+  // an immediate 9216*(2*ks2) + 1024*(nt >> 1) and one of four per-lane bases
+  // tr_base[nt & 1][half] (which hold the row group of the half).
   const int ti = lane & 15, th = (lane >> 4) & 1;
   const int tr_r = ti >> 2, tr_x = 2 * th + ((ti & 3) >> 1), tr_piece = ti & 1;
-  const int tr_base = (4 * g + tr_r) * ROW_BYTES + ((tr_x ^ (2 * g + (tr_r >> 1))) << 4) + (tr_piece << 3);
+  int tr_base[2][2];
+#pragma unroll
+  for (int odd = 0; odd < 2; ++odd)
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+      tr_base[odd][half] = tile_off(8 * half + 4 * g + tr_r, 32 * dh + 4 * odd + tr_x) + 8 * tr_piece;
 
-  __syncthreads();  // prow ready
+  // prow ready; does any row need masking beyond a partial last tile?
+  const bool any_bad = __syncthreads_or(bad) != 0;
   const int ntiles = (nrows + MLA_T - 1) / MLA_T;
-  if (ntiles > 0) issue_tile(a.kv, prow, 0, nrows, tb0, wave, lane);
-  if (ntiles > 1) issue_tile(a.kv, prow, MLA_T, nrows, tb1, wave, lane);
+  // Buffer descriptor of the latent cache from row brow on.
+  const uint32_t brow = __builtin_amdgcn_readfirstlane(
+      (!WIDE && a.map.block_shift < 0) ? (uint32_t)a.map.seq_row0[seq] : 0u);
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(a.kv + (size_t)brow * 576), (short)0, 0xFFFFFFFF, 0x00020000);
+  if (ntiles > 0) issue_tile<WIDE>(rs, a.kv, brow, prow, 0, true, tb0, wave, lane);
+  if (ntiles > 1) issue_tile<WIDE>(rs, a.kv, brow, prow, MLA_T, true, tb1, wave, lane);
 
   // One tile: wait for it, start the gather of tile t + 2 into nbuf, compute.
   auto tile_step = [&](const int t, const uint8_t *buf, uint8_t *nbuf) {
@@ -223,98 +308,147 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     // The buffer of tile t-1 is free now (every wave is past its compute):
-    // start tile t + 2 into it.
-    if (t + 2 < ntiles) issue_tile(a.kv, prow, (t + 2) * MLA_T, nrows, nbuf, wave, lane);
+    // tile t + 2 goes into it.  Past the last
+    // tile the parts still issue (no branch between the MFMAs, which would
+    // make the compiler drain the LDS read ring), but all read one row of
+    // this block, which stays in cache, into the free buffer.
+    const bool next2 = t + 2 < ntiles;
     const int t0 = t * MLA_T;
+    issue_tile<WIDE>(rs, a.kv, brow, prow, t0 + 2 * MLA_T, next2, nbuf, wave, lane);
+    __builtin_amdgcn_sched_barrier(0);
 
-    // S^T[row, head] for 32 rows x 32 heads.
+    // S^T[row, head] for 32 rows x the 32 own heads.
     // K fragments are read QK_AHEAD steps ahead of their MFMA (ring buffer).
     v16f s;
-    constexpr int QK_AHEAD = 3;
+    constexpr int QK_AHEAD = 4;
     uint4 kf[QK_AHEAD + 1];
 #pragma unroll
     for (int ks = 0; ks < QK_AHEAD; ++ks)
-      kf[ks] = *reinterpret_cast<const uint4 *>(buf + qk_base[ks & 3] + 128 * (ks >> 2));
+      kf[ks] = *reinterpret_cast<const uint4 *>(buf + qk_base[ks & 3] + 1024 * (ks >> 2));
 #pragma unroll
     for (int ks = 0; ks < 36; ++ks) {
       if (ks + QK_AHEAD < 36)
         kf[(ks + QK_AHEAD) % (QK_AHEAD + 1)] =
-            *reinterpret_cast<const uint4 *>(buf + qk_base[(ks + QK_AHEAD) & 3] + 128 * ((ks + QK_AHEAD) >> 2));
+            *reinterpret_cast<const uint4 *>(buf + qk_base[(ks + QK_AHEAD) & 3] + 1024 * ((ks + QK_AHEAD) >> 2));
       if (ks == 0)
         mfma_s_first(s, kf[0], qb[0]);
       else
         mfma_s(s, kf[ks % (QK_AHEAD + 1)], qb[ks]);
+      // Keep the written order: the scheduler would otherwise sink each read
+      // next to its MFMA and undo the prefetch distance.
+      __builtin_amdgcn_sched_barrier(0);
     }
     mfma_s_drain(s);
 
-    // Online softmax for head c over this tile's rows 8i + 4g + j.
+    // Online softmax for own head c over this tile's rows 8i + 4g + j, in
+    // log2 units: z = scale_log2 * s, folded into the exp2 argument below
+    // (scale_log2 > 0, so the max of z is scale_log2 times the max of s).
+    // Only a partial last tile, or a block whose list holds positions outside
+    // [0, n_vis), masks rows to -inf.
     float z[16];
-    float tmax = -INFINITY;
+    float zscale, tmax;
+    if (!any_bad && t0 + MLA_T <= nrows) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rbase = t0 + 8 * i + 4 * g;
-      const uint4 pr = *reinterpret_cast<const uint4 *>(&prow[rbase]);
-      const uint32_t prv[4] = {pr.x, pr.y, pr.z, pr.w};
+      for (int i = 0; i < 16; ++i) z[i] = s[i];
+      float m5[5];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bool ok = (rbase + j < nrows) && !(prv[j] & INVALID_ROW);
-        const float v = ok ? s[4 * i + j] * p.scale_log2 : -INFINITY;
-        z[4 * i + j] = v;
-        tmax = fmaxf(tmax, v);
+      for (int i = 0; i < 5; ++i) m5[i] = max3f(z[3 * i], z[3 * i + 1], z[3 * i + 2]);
+      const float ma = max3f(m5[0], m5[1], m5[2]), mb = max3f(m5[3], m5[4], z[15]);
+      tmax = xhalf_max(max3f(ma, mb, mb)) * p.scale_log2;
+      zscale = p.scale_log2;
+    } else {
+      tmax = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rbase = t0 + 8 * i + 4 * g;
+        const uint4 pr = *reinterpret_cast<const uint4 *>(&prow[rbase]);
+        const uint32_t prv[4] = {pr.x, pr.y, pr.z, pr.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bool ok = (rbase + j < nrows) && !(prv[j] & INVALID_ROW);
+          const float v = ok ? s[4 * i + j] * p.scale_log2 : -INFINITY;
+          z[4 * i + j] = v;
+          tmax = fmaxf(tmax, v);
+        }
       }
+      tmax = xhalf_max(tmax);
+      zscale = 1.0f;
     }
-    tmax = fmaxf(tmax, shfl_xor(tmax, 32));
     // The reference max moves only when a head's tile max exceeds it by more
     // than RESCALE_LOG2 (always on the first tile with a valid row), so P <=
     // 2^RESCALE_LOG2 and O is rescaled rarely.  An all-masked tile changes nothing.
-    if (__ballot(tmax > m_ref + RESCALE_LOG2) != 0ull) {
+    const bool resc = __ballot(tmax > m_ref + RESCALE_LOG2) != 0ull;
+    if (resc) {
       const float m_new = fmaxf(m_ref, tmax);
       const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);  // 0 while m_ref = -inf
       l_run *= alpha;
       m_ref = m_new;
-      if (t > 0) {  // O is still zero on the first tile
-        if (g == 0) xch[wave][c] = alpha;
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        float al[16];
-        read_head_values(xch[wave], g, al);
-#pragma unroll
-        for (int nt = 0; nt < 16; ++nt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            float x = o[nt][i];
-            scale_acc(x, al[i]);
-            o[nt][i] = x;
-          }
-        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-      }
+      if (g == 0) aex[wave][c] = alpha;
     }
-    const float mref = (m_ref == -INFINITY) ? 0.0f : m_ref;  // all rows so far masked: z = -inf, p = 0
-    float psum = 0.0f;
+    if (lane == 0) fex[wave] = resc ? 1 : 0;
+    const float nmref = (m_ref == -INFINITY) ? 0.0f : -m_ref;  // all rows so far masked: z = -inf, p = 0
+    float ps[8];
     uint32_t pk[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float e0 = __builtin_amdgcn_exp2f(z[2 * i] - mref);
-      const float e1 = __builtin_amdgcn_exp2f(z[2 * i + 1] - mref);
-      psum += e0 + e1;
+      const float e0 = __builtin_amdgcn_exp2f(fmaf(z[2 * i], zscale, nmref));
+      const float e1 = __builtin_amdgcn_exp2f(fmaf(z[2 * i + 1], zscale, nmref));
+      ps[i] = e0 + e1;
       pk[i] = pack_bf16(e0, e1);
     }
-    l_run += psum;
+    l_run += ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
+    const uint4 pa0 = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    const uint4 pa1 = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+    pex[wave][0][lane] = pa0;
+    pex[wave][1][lane] = pa1;
 
-    // O += P . V over the tile's 32 rows (2 k-steps of 16).  The k-slots of
-    // lane group g in step ks2 are rows 16*ks2 + 4g + {0..3} and
-    // 16*ks2 + 8 + 4g + {0..3} (where the S^T accumulator put them); the
+    // Publish P and the rescale factors to the partner: LDS writes done, then
+    // the barrier (bare, so the DMA of tiles t+1 and t+2 stays in flight).
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    const uint4 pp0 = pex[partner][0][lane];
+    const uint4 pp1 = pex[partner][1][lane];
+    if (t > 0) {  // O is still zero on the first tile
+      float al[16];
+      if (resc) {
+        read_head_values(aex[wave], g, al);
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            float x = o[0][nt][i];
+            scale_acc(x, al[i]);
+            o[0][nt][i] = x;
+          }
+      }
+      if (fex[partner]) {
+        read_head_values(aex[partner], g, al);
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            float x = o[1][nt][i];
+            scale_acc(x, al[i]);
+            o[1][nt][i] = x;
+          }
+      }
+    }
+
+    // O += P . V over the tile's 32 rows (2 k-steps of 16), for both head
+    // sets of the pair; each V fragment feeds two MFMAs.  The k-slots of lane
+    // group g in step ks2 are rows 16*ks2 + 4g + {0..3} and 16*ks2 + 8 + 4g +
+    // {0..3} (where the S^T accumulator put them, in both wavefronts); the
     // transposing read gives lane l the 4 rows of one of those sets at column
     // n = l % 32: lanes 4r..4r+3 of each 16-lane group point at row r of the
-    // set, 4 columns each.
-    // 32 steps j = (ks2, nt); the B fragment of step j is read PV_AHEAD steps
-    // ahead of its MFMA (ring buffer).
-    constexpr int PV_AHEAD = 2;
+    // set, 4 columns each.  16 steps j = (ks2, nt); the B fragment of step j
+    // is read PV_AHEAD steps ahead of its MFMAs (ring buffer).
+    constexpr int PV_AHEAD = 4;
     auto v_frag = [&](int j) {
-      const int ks2 = j >> 4, nt = j & 15;
-      const int off0 = tr_base + (16 * ks2) * ROW_BYTES + 64 * nt;            // half 0
-      const int off1 = tr_base + (16 * ks2 + 8) * ROW_BYTES + 64 * (nt ^ 1);  // half 1
+      const int ks2 = j >> 3, nt = j & 7;
+      const int off0 = tr_base[nt & 1][0] + 9216 * (2 * ks2) + 1024 * (nt >> 1);  // half 0
+      const int off1 = tr_base[nt & 1][1] + 9216 * (2 * ks2) + 1024 * (nt >> 1);  // half 1
       const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)(buf + off0));
       const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)(buf + off1));
       const uint2 ulo = __builtin_bit_cast(uint2, lo), uhi = __builtin_bit_cast(uint2, hi);
@@ -323,14 +457,14 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
     uint4 vf[PV_AHEAD + 1];
 #pragma unroll
     for (int j = 0; j < PV_AHEAD; ++j) vf[j] = v_frag(j);
-    const uint4 pa0 = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-    const uint4 pa1 = make_uint4(pk[4], pk[5], pk[6], pk[7]);
 #pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      if (j + PV_AHEAD < 32) vf[(j + PV_AHEAD) % (PV_AHEAD + 1)] = v_frag(j + PV_AHEAD);
-      const int nt = j & 15;
-      o[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(j < 16 ? pa0 : pa1), as_bf(vf[j % (PV_AHEAD + 1)]),
-                                                      o[nt], 0, 0, 0);
+    for (int j = 0; j < 16; ++j) {
+      if (j + PV_AHEAD < 16) vf[(j + PV_AHEAD) % (PV_AHEAD + 1)] = v_frag(j + PV_AHEAD);
+      const int nt = j & 7;
+      const v8bf vb = as_bf(vf[j % (PV_AHEAD + 1)]);
+      o[0][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(j < 8 ? pa0 : pa1), vb, o[0][nt], 0, 0, 0);
+      o[1][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(j < 8 ? pp0 : pp1), vb, o[1][nt], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
   for (int t = 0; t < ntiles; t += NBUF) {
@@ -338,23 +472,30 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
     if (t + 1 < ntiles) tile_step(t + 1, tb1, tb0);
     if (t + 2 < ntiles) tile_step(t + 2, tb2, tb1);
   }
+  // The last two tiles issued gathers past the end: let them land before the
+  // block's LDS can be handed to another block.
+  __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0)
 
-  // Normalise.  Both lane halves hold partial sums of head c.
-  const float l_tot = l_run + shfl_xor(l_run, 32);
+  // Normalise.  Both lane halves hold partial sums of own head c; the pair
+  // exchanges 1/l so that each wavefront can scale its partner's head rows.
+  const float l_tot = xhalf_sum(l_run);
   const float inv = (l_tot > 0.0f) ? 1.0f / l_tot : 0.0f;
   const float lse_v = (l_tot > 0.0f) ? m_ref * LN2 + logf(l_tot) : -INFINITY;
-  if (g == 0) xch[wave][c] = inv;
+  if (g == 0) aex[wave][c] = inv;
   __syncthreads();
-  float il[16];
-  read_head_values(xch[wave], g, il);
 #pragma unroll
-  for (int nt = 0; nt < 16; ++nt)
+  for (int mt = 0; mt < 2; ++mt) {
+    float il[16];
+    read_head_values(aex[mt == 0 ? wave : partner], g, il);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float x = o[nt][i];
-      scale_acc(x, il[i]);
-      o[nt][i] = x;
-    }
+    for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float x = o[mt][nt][i];
+        scale_acc(x, il[i]);
+        o[mt][nt][i] = x;
+      }
+  }
 
   float *obase;
   float *lbase;
@@ -366,14 +507,18 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
     lbase = p.part_lse + ((int64_t)q * p.nsplit + sp) * 128;
   }
 #pragma unroll
-  for (int nt = 0; nt < 16; ++nt)
+  for (int mt = 0; mt < 2; ++mt) {
+    const int hset = 32 * (mt == 0 ? wave : partner);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int h = 32 * wave + 8 * i + 4 * g + j;
-        obase[(int64_t)h * 512 + 32 * nt + c] = o[nt][4 * i + j];
-      }
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int h = hset + 8 * i + 4 * g + j;
+          obase[(int64_t)h * 512 + 256 * dh + 32 * nt + c] = o[mt][nt][4 * i + j];
+        }
+  }
   if (lbase && g == 0) lbase[head] = lse_v;
 }
 
@@ -438,7 +583,13 @@ hipError_t launch_mla(const MlaLaunch &a, bool decode, void *ws, hipStream_t st)
     p.part_o = static_cast<float *>(ws);
     p.part_lse = p.part_o + (size_t)a.num_q * p.nsplit * 128 * 512;
   }
-  hipLaunchKernelGGL(mla_kernel, dim3((unsigned)((int64_t)a.num_q * p.nsplit)), dim3(MLA_THREADS), 0, st, p);
+  // Offsets from the descriptor base stay below 4 GiB unless a paged pool is that large.
+  const bool wide = a.map.block_shift >= 0 && a.num_rows * (int64_t)ROW_BYTES >= 0xFFFFF000ll - ROW_BYTES;
+  const dim3 grid((unsigned)((int64_t)a.num_q * p.nsplit));
+  if (wide)
+    hipLaunchKernelGGL(mla_kernel<true>, grid, dim3(MLA_THREADS), 0, st, p);
+  else
+    hipLaunchKernelGGL(mla_kernel<false>, grid, dim3(MLA_THREADS), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.nsplit == 1) return e;
   hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)((int64_t)a.num_q * 64)), dim3(256), 0, st, p.part_o,
