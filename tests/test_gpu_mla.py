@@ -113,3 +113,36 @@ def test_index_order_does_not_matter():
     ov = OracleView(wl)
     o_ref, l_ref = ov.mla(0, idx[0])
     check_out(b[0], o_ref, lb[0], l_ref, "permuted")
+
+
+@pytest.mark.parametrize("decode", [True, False])
+def test_paged_pool_beyond_4gib(decode):
+    """A paged latent pool of 4.4 GB (more than 4 GiB of rows) whose block
+    table alternates blocks at the start and at the end of the pool, so that
+    row offsets no longer fit in 32 bits."""
+    from types import SimpleNamespace
+    banner(f"mla paged pool > 4 GiB decode={decode}")
+    bs, nblocks = 64, 59392                     # 3,801,088 rows x 1152 bytes = 4.38 GB
+    rows = bs * nblocks
+    seq_len, nseq = 4096, 2
+    per_seq = seq_len // bs
+    low = np.arange(nseq * per_seq // 2)
+    high = nblocks - 1 - np.arange(nseq * per_seq // 2)
+    order = np.empty(nseq * per_seq, np.int64)
+    order[0::2], order[1::2] = low, high        # neighbours in a sequence lie ~4.3 GB apart
+    table = order.reshape(nseq, per_seq).astype(np.int32)
+    kv = torch.empty((rows, 576), dtype=torch.bfloat16, device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(77)
+    for b in order:
+        kv[b * bs:(b + 1) * bs] = torch.randn((bs, 576), generator=g, device="cuda").to(torch.bfloat16)
+    q_mla = torch.randn((nseq, 128, 576), generator=g, device="cuda").to(torch.bfloat16)
+    wl = SimpleNamespace(
+        name="paged pool 4.4 GB", nq=nseq, num_seqs=nseq, rows=rows, kv=kv, q_mla=q_mla,
+        q_seq=torch.arange(nseq, dtype=torch.int32, device="cuda"),
+        q_nvis=torch.full((nseq,), seq_len, dtype=torch.int32, device="cuda"), max_nvis=seq_len,
+        block_size=bs, block_table=torch.from_numpy(table).cuda(), row0=None, softmax_scale=192 ** -0.5)
+    idx, cnt = random_selection(wl, 2048, 9)
+    compare(wl, idx, cnt, 2048, decode)
+    del kv
+    torch.cuda.empty_cache()
