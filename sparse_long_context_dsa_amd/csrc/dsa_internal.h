@@ -45,19 +45,23 @@ struct IndexerLaunch {
 hipError_t launch_indexer(const IndexerLaunch &a, hipStream_t st);
 
 // Top-k: radix digits of 11/11/10 bits; rows up to TOPK_ROW_MAX are selected
-// by one block from LDS, longer rows in chunks of TOPK_CHUNK.
+// by one block from registers and LDS, longer rows by blocks of TOPK_LONG_SPAN
+// positions that stream the row once, the last of them finishing the row.
 constexpr int TOPK_BINS = 2048;
 constexpr int TOPK_ROW_MAX = 16384;
-constexpr int TOPK_CHUNK = 16384;
-constexpr int TOPK_MAX_CHUNKS = 64;  // histories up to 2^20 positions
+constexpr int TOPK_CHUNK = 16384;      // score chunk of the standalone first-digit histogram
+constexpr int TOPK_MAX_CHUNKS = 64;    // histories up to 2^20 positions
 constexpr int MAX_NVIS = TOPK_CHUNK * TOPK_MAX_CHUNKS;
+constexpr int TOPK_LONG_WAVES = 16;    // wavefronts of a long-row block
+constexpr int TOPK_WAVE_SPAN = 2048;   // positions per wavefront (4 rounds of 512)
+constexpr int TOPK_LONG_SPAN = TOPK_LONG_WAVES * TOPK_WAVE_SPAN;  // 32768 positions per block
 struct TopkWs {
-  uint32_t *hist;     // [num_q, TOPK_BINS] first-digit histogram
-  uint32_t *hist2;    // [num_q, TOPK_BINS] second-digit histogram (long rows)
-  uint32_t *done;     // [num_q] blocks finished per query (long rows)
-  uint32_t *ccount;   // [num_q, nchunks]
-  uint2 *cand;        // [num_q, nchunks, TOPK_CHUNK] (key, position) candidates
-  int32_t nchunks;    // 0 when every row fits TOPK_ROW_MAX
+  uint32_t *hist;     // [num_q, TOPK_BINS] first-digit histogram (cleared each call)
+  uint2 *b1info;      // [num_q] long rows: (first-digit threshold bin B1, keys above B1)
+  uint32_t *wcnt;     // [num_q, nblk, TOPK_LONG_WAVES] candidates per wavefront
+  uint2 *cand;        // [num_q, nblk, TOPK_LONG_WAVES, TOPK_WAVE_SPAN] (key, position)
+  int32_t nblk;       // long-row blocks per query (0 when every row fits TOPK_ROW_MAX)
+  int32_t nchunks;    // score chunks per row for the standalone histogram
 };
 size_t topk_ws_bytes(int num_q, int max_nvis);
 TopkWs topk_ws_carve(void *ws, int num_q, int max_nvis);

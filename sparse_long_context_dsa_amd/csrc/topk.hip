@@ -26,15 +26,18 @@
 //    per query; only the histograms live in LDS, so many rows are selected per
 //    CU at once.  The first-digit histogram comes from the indexer's fused
 //    epilogue when available, else from LDS atomics.
-//  * topk_chunk_kernel + topk_final_kernel (longer rows, e.g. 128K decode):
-//    chunk blocks stream the scores once, find the threshold bin B1 from the
-//    first-digit histogram, compact the candidates (digit >= B1, about
-//    k + |B1| of them) into per-chunk lists in position order and add the
-//    second-digit histogram of the B1 keys into a global one; then one block
-//    per query loads the histograms and all candidate lists into LDS with
-//    independent loads and finishes there (from global memory if the lists do
-//    not fit).  The kernel boundary publishes the lists, so no block-level
-//    device-scope fences are needed.
+//  * longer rows (e.g. 128K decode): the row kernel's block of such a row
+//    finds the threshold bin B1 of the first digit (and the count above it)
+//    from the histogram built with the scores; topk_long_kernel blocks of 16
+//    wavefronts, each owning 32768 consecutive positions (2048 per
+//    wavefront), stream the scores once and append the candidates (digit >=
+//    B1, about k + |B1| per row) to per-wavefront lists in position order,
+//    ranks from ballots; topk_finish_kernel (one block per long row, after
+//    the kernel boundary has published the lists) loads the lists into LDS in
+//    position order and finishes there: digits 2 and 3 as LDS histograms of
+//    the candidates, then the output as a position-ordered compaction.  (Handing the row to its last block inside
+//    one kernel would need an agent-scope fence per block, which on this
+//    part writes back and invalidates the XCD's L2 and costs far more.)
 #include "device_util.h"
 #include "dsa_internal.h"
 
@@ -45,9 +48,10 @@ constexpr int TK_ROUNDS = 8;                                  // rounds per bloc
 constexpr int TK_J = TOPK_ROW_MAX / (TK_THREADS * TK_ROUNDS);  // 8 scores per thread per round
 constexpr int TK_PER = TK_ROUNDS * TK_J;                      // 64 keys per thread
 constexpr int TK_ROUND_SPAN = TK_THREADS * TK_J;              // 2048 positions per round
-constexpr int FIN_THREADS = 1024;
-constexpr int LIST_CAP = 8192;  // candidates the finalize keeps in LDS
-static_assert(TOPK_CHUNK == TOPK_ROW_MAX, "one block covers one chunk");
+constexpr int LONG_THREADS = TOPK_LONG_WAVES * WAVE;
+constexpr int LONG_ROUNDS = TOPK_WAVE_SPAN / 512;  // rounds of 512 positions per wavefront
+constexpr int TAIL_CAP = 12288;                     // candidates the finishing block keeps in LDS
+static_assert(TOPK_CHUNK == TOPK_ROW_MAX, "one histogram block covers one chunk");
 static_assert(TK_J == 8, "two float4 loads per round");
 
 static inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -55,24 +59,28 @@ static inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 static inline int topk_nchunks(int max_nvis) {
   return max_nvis <= TOPK_ROW_MAX ? 0 : (max_nvis + TOPK_CHUNK - 1) / TOPK_CHUNK;
 }
+static inline int topk_nblk(int max_nvis) {
+  return max_nvis <= TOPK_ROW_MAX ? 0 : (max_nvis + TOPK_LONG_SPAN - 1) / TOPK_LONG_SPAN;
+}
 
 size_t topk_ws_bytes(int num_q, int max_nvis) {
-  const size_t nq = (size_t)num_q;
-  const size_t nc = (size_t)topk_nchunks(max_nvis);
-  return align256(nq * (2 * TOPK_BINS + 1) * 4) + align256(nq * nc * 4) + nq * nc * TOPK_CHUNK * sizeof(uint2);
+  const size_t nq = (size_t)num_q, nb = (size_t)topk_nblk(max_nvis);
+  return align256(nq * TOPK_BINS * 4) + align256(nq * sizeof(uint2)) +
+         align256(nq * nb * TOPK_LONG_WAVES * 4) + nq * nb * TOPK_LONG_SPAN * sizeof(uint2);
 }
 
 TopkWs topk_ws_carve(void *ws, int num_q, int max_nvis) {
   TopkWs w;
   const size_t nq = (size_t)num_q;
   w.nchunks = topk_nchunks(max_nvis);
+  w.nblk = topk_nblk(max_nvis);
   uint8_t *p = static_cast<uint8_t *>(ws);
-  w.hist = reinterpret_cast<uint32_t *>(p);  // [nq, 2048] first digit
-  w.hist2 = w.hist + nq * TOPK_BINS;         // [nq, 2048] second digit
-  w.done = w.hist2 + nq * TOPK_BINS;         // [nq] (unused; cleared with the histograms)
-  p += align256(nq * (2 * TOPK_BINS + 1) * 4);
-  w.ccount = reinterpret_cast<uint32_t *>(p);
-  p += align256(nq * w.nchunks * 4);
+  w.hist = reinterpret_cast<uint32_t *>(p);  // [nq, 2048] first digit (cleared each call)
+  p += align256(nq * TOPK_BINS * 4);
+  w.b1info = reinterpret_cast<uint2 *>(p);   // [nq] written before it is read
+  p += align256(nq * sizeof(uint2));
+  w.wcnt = reinterpret_cast<uint32_t *>(p);
+  p += align256(nq * w.nblk * TOPK_LONG_WAVES * 4);
   w.cand = reinterpret_cast<uint2 *>(p);
   return w;
 }
@@ -245,17 +253,26 @@ __global__ __launch_bounds__(TK_THREADS) void topk_row_kernel(SelectArgs a) {
   const int q = blockIdx.x;
   const int n = a.q_nvis[q];
   const int k = a.k;
-  if (n > TOPK_ROW_MAX) return;
-  int32_t *out = a.idx + (int64_t)q * k;
-  if (n <= k) {
-    write_short(out, a.count, q, n, k, TK_THREADS);
-    return;
-  }
   __shared__ uint32_t h[TOPK_BINS];
   __shared__ int sm[TK_THREADS / WAVE];
   __shared__ uint64_t sm64[TK_THREADS / WAVE];
   __shared__ int res[2];
   const int t = threadIdx.x;
+  if (n > TOPK_ROW_MAX) {
+    // A long row: only its first-digit threshold bin, once, for the stream
+    // blocks and the finish of this row.
+    const uint32_t *gh = a.ws.hist + (int64_t)q * TOPK_BINS;
+    for (int b = t; b < TOPK_BINS; b += TK_THREADS) h[b] = gh[b];
+    __syncthreads();
+    find_rank_bin<TK_THREADS, TOPK_BINS>(h, k, sm, res);
+    if (t == 0) a.ws.b1info[q] = make_uint2((uint32_t)res[0], (uint32_t)res[1]);
+    return;
+  }
+  int32_t *out = a.idx + (int64_t)q * k;
+  if (n <= k) {
+    write_short(out, a.count, q, n, k, TK_THREADS);
+    return;
+  }
   uint32_t key[TK_PER];
   load_keys(a.scores + (int64_t)q * a.ld, 0, n, key);
   // Digit 1: key[31:21].
@@ -350,167 +367,211 @@ __global__ __launch_bounds__(TK_THREADS) void topk_row_kernel(SelectArgs a) {
   if (t == 0 && a.count) a.count[q] = min(tot, k);
 }
 
-__global__ __launch_bounds__(TK_THREADS) void topk_chunk_kernel(SelectArgs a) {
-  const int nchunks = a.ws.nchunks;
-  const int q = blockIdx.x / nchunks;
-  const int c = blockIdx.x - q * nchunks;
+// Lanes below this one in the wavefront (mbcnt over a ballot mask).
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+// Exclusive prefix over the wavefront of c (0 <= c < 16) and the wave total,
+// from one ballot per bit: no cross-lane data movement through LDS.
+__device__ __forceinline__ int wave_excl_small(int c, int &total) {
+  int ex = 0, tot = 0;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const uint64_t m = __ballot((c >> b) & 1);
+    ex += lanes_below(m) << b;
+    tot += __popcll(m) << b;
+  }
+  total = tot;
+  return ex;
+}
+
+__global__ __launch_bounds__(LONG_THREADS) void topk_long_kernel(SelectArgs a) {
+  const int nblk = a.ws.nblk;
+  const int q = blockIdx.x / nblk;
+  const int c = blockIdx.x - q * nblk;
   const int n = a.q_nvis[q];
   const int k = a.k;
-  if (n <= TOPK_ROW_MAX) return;
-  const int start = c * TOPK_CHUNK;
-  if (start >= n) return;
-
-  __shared__ uint32_t h[TOPK_BINS];
-  __shared__ int sm[TK_THREADS / WAVE];
-  __shared__ uint64_t sm64[TK_THREADS / WAVE];
-  __shared__ int res[2];
+  if (n <= TOPK_ROW_MAX) return;  // topk_row_kernel
+  const int nb = (n + TOPK_LONG_SPAN - 1) / TOPK_LONG_SPAN;
+  if (c >= nb) return;
   const int t = threadIdx.x;
-  uint32_t key[TK_PER];
-  load_keys(a.scores + (int64_t)q * a.ld, start, n, key);  // in flight while the histogram is read
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & (WAVE - 1);
+  const int p0 = c * TOPK_LONG_SPAN + wave * TOPK_WAVE_SPAN;
+  const int p1 = min(n, p0 + TOPK_WAVE_SPAN);
+  const float *row = a.scores + (int64_t)q * a.ld;
 
-  // Threshold bin B1 from the first-digit histogram.
-  const uint32_t *gh1 = a.ws.hist + (int64_t)q * TOPK_BINS;
-  for (int b = t; b < TOPK_BINS; b += TK_THREADS) h[b] = gh1[b];
-  __syncthreads();
-  find_rank_bin<TK_THREADS, TOPK_BINS>(h, k, sm, res);
-  const uint32_t b1 = (uint32_t)res[0];
-  __syncthreads();
-  zero_lds<TK_THREADS>(h, TOPK_BINS);
-  __syncthreads();
-
-  // Candidates (digit >= B1) in position order; second-digit histogram of B1.
-  Packed fc{0, 0};
+  // All score loads first.  Lane l reads positions p0 + 512 u + 8 l .. +7 of
+  // round u; a float4 at a position < p1 stays inside the row (ld % 4 == 0),
+  // past p1 it reads position 0 and the keys become 0, below B1.
+  float4 f[LONG_ROUNDS][2];
 #pragma unroll
-  for (int rr = 0; rr < TK_ROUNDS; ++rr) {
+  for (int u = 0; u < LONG_ROUNDS; ++u)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int ii = p0 + 512 * u + 8 * lane + 4 * hh;
+      f[u][hh] = *reinterpret_cast<const float4 *>(row + (ii < p1 ? ii : 0));
+    }
+
+  const uint32_t b1 = a.ws.b1info[q].x;  // threshold bin B1 (row kernel)
+
+  // Candidates in position order.
+  uint2 *lst = a.ws.cand + (((int64_t)q * nblk + c) * TOPK_LONG_WAVES + wave) * TOPK_WAVE_SPAN;
+  int wc = 0;  // wave-uniform
+#pragma unroll
+  for (int u = 0; u < LONG_ROUNDS; ++u) {
+    const int i0 = p0 + 512 * u + 8 * lane;
+    const float v[8] = {f[u][0].x, f[u][0].y, f[u][0].z, f[u][0].w, f[u][1].x, f[u][1].y, f[u][1].z, f[u][1].w};
+    uint32_t key[8];
     int cnt = 0;
 #pragma unroll
-    for (int j = 0; j < TK_J; ++j) {
-      const uint32_t kk = key[TK_J * rr + j];
-      cnt += ((kk >> 21) >= b1) ? 1 : 0;
-      if ((kk >> 21) == b1) atomicAdd(&h[(kk >> 10) & 2047u], 1u);
+    for (int j = 0; j < 8; ++j) {
+      key[j] = (i0 + j < p1) ? order_key(v[j]) : 0u;
+      cnt += ((key[j] >> 21) >= b1) ? 1 : 0;
     }
-    pack_add(fc, rr, cnt);
-  }
-  int off[TK_ROUNDS];
-  const int total = ordered_offsets(fc, sm64, off);  // its barriers also complete the histogram
-  uint2 *glst = a.ws.cand + ((int64_t)q * nchunks + c) * TOPK_CHUNK;
+    int tot;
+    int pos = wc + wave_excl_small(cnt, tot);
 #pragma unroll
-  for (int rr = 0; rr < TK_ROUNDS; ++rr) {
-    int pos = off[rr];
-#pragma unroll
-    for (int j = 0; j < TK_J; ++j) {
-      const uint32_t kk = key[TK_J * rr + j];
-      if ((kk >> 21) >= b1) glst[pos++] = make_uint2(kk, (uint32_t)(start + slot_pos(t, rr, j)));
-    }
+    for (int j = 0; j < 8; ++j)
+      if ((key[j] >> 21) >= b1) lst[pos++] = make_uint2(key[j], (uint32_t)(i0 + j));
+    wc += tot;
   }
-  if (t == 0) a.ws.ccount[(int64_t)q * nchunks + c] = (uint32_t)total;
-  uint32_t *g2 = a.ws.hist2 + (int64_t)q * TOPK_BINS;
-  for (int b = t; b < TOPK_BINS; b += TK_THREADS)
-    if (h[b]) atomicAdd(&g2[b], h[b]);
+  if (lane == 0) a.ws.wcnt[((int64_t)q * nblk + c) * TOPK_LONG_WAVES + wave] = (uint32_t)wc;
 }
 
-// Finds the chunk holding candidate i, given the exclusive prefix off[0..nc].
-__device__ __forceinline__ int locate(const int *off, int nc, int i) {
-  int c = 0;
-  while (c + 1 < nc && off[c + 1] <= i) ++c;
-  return c;
-}
-
-__global__ __launch_bounds__(FIN_THREADS) void topk_final_kernel(SelectArgs a) {
-  const int nchunks = a.ws.nchunks;
+__global__ __launch_bounds__(LONG_THREADS) void topk_finish_kernel(SelectArgs a) {
+  const int nblk = a.ws.nblk;
   const int q = blockIdx.x;
   const int n = a.q_nvis[q];
   const int k = a.k;
-  if (n <= TOPK_ROW_MAX) return;
-  const int nc = (n + TOPK_CHUNK - 1) / TOPK_CHUNK;
-
-  __shared__ uint2 lst[LIST_CAP];
-  __shared__ uint32_t h1[TOPK_BINS];
-  __shared__ uint32_t h2[TOPK_BINS];
-  __shared__ int sm[FIN_THREADS / WAVE];
+  if (n <= TOPK_ROW_MAX) return;  // topk_row_kernel
+  const int nb = (n + TOPK_LONG_SPAN - 1) / TOPK_LONG_SPAN;
+  __shared__ uint32_t h[TOPK_BINS];
+  __shared__ int sm[LONG_THREADS / WAVE];
   __shared__ int res[2];
-  __shared__ int off[TOPK_MAX_CHUNKS + 1];
+  __shared__ uint2 tl[TAIL_CAP];
+  __shared__ int off[TOPK_MAX_CHUNKS / 2 * TOPK_LONG_WAVES + 1];
   const int t = threadIdx.x;
 
   // Everything that does not depend on anything else is requested at once.
-  const uint32_t *gh1 = a.ws.hist + (int64_t)q * TOPK_BINS;
-  const uint32_t *gh2 = a.ws.hist2 + (int64_t)q * TOPK_BINS;
-  for (int b = t; b < TOPK_BINS; b += FIN_THREADS) {
-    h1[b] = gh1[b];
-    h2[b] = gh2[b];
+  const uint2 bi = a.ws.b1info[q];
+  const uint32_t b1 = bi.x;
+  const int r = k - (int)bi.y;
+  const int nseg = nb * TOPK_LONG_WAVES;  // lists in position order: (block, wavefront)
+  zero_lds<LONG_THREADS>(h, TOPK_BINS);
+  const uint32_t *gw = a.ws.wcnt + (int64_t)q * nblk * TOPK_LONG_WAVES;
+  {
+    static_assert(TOPK_MAX_CHUNKS / 2 * TOPK_LONG_WAVES <= LONG_THREADS, "one list count per thread");
+    int tot;
+    const int ex = block_exclusive_scan<LONG_THREADS>(t < nseg ? (int)gw[t] : 0, sm, tot);
+    if (t < nseg) off[t] = ex;
+    if (t == 0) off[nseg] = tot;
   }
-  if (t < nc) off[t + 1] = (int)a.ws.ccount[(int64_t)q * nchunks + t];
   __syncthreads();
-  if (t == 0) {
-    off[0] = 0;
-    for (int cc = 1; cc <= nc; ++cc) off[cc] += off[cc - 1];
+  const int ntot = off[nseg];
+  const uint2 *cq = a.ws.cand + (int64_t)q * nblk * TOPK_LONG_SPAN;
+  const bool in_lds = ntot <= TAIL_CAP;
+  // Candidate i lives in list s (off[s] <= i < off[s+1]) at index i - off[s].
+  auto locate = [&](int i) {
+    int lo = 0, hi = nseg;  // largest s with off[s] <= i
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (off[mid] <= i) lo = mid; else hi = mid;
+    }
+    return cq[(int64_t)lo * TOPK_WAVE_SPAN + (i - off[lo])];
+  };
+  if (in_lds)
+    for (int i = t; i < ntot; i += LONG_THREADS) tl[i] = locate(i);
+  __syncthreads();
+  auto get = [&](int i) { return in_lds ? tl[i] : locate(i); };
+  // Digit 2: key[20:10] of the candidates in bin B1.
+  for (int i = t; i < ntot; i += LONG_THREADS) {
+    const uint32_t kk = get(i).x;
+    if ((kk >> 21) == b1) atomicAdd(&h[(kk >> 10) & 2047u], 1u);
   }
-  find_rank_bin<FIN_THREADS, TOPK_BINS>(h1, k, sm, res);  // its barriers publish off[]
-  const uint32_t b1 = (uint32_t)res[0];
-  const int r = k - res[1];
   __syncthreads();
-  find_rank_bin<FIN_THREADS, TOPK_BINS>(h2, r, sm, res);
+  find_rank_bin<LONG_THREADS, TOPK_BINS>(h, r, sm, res);
   const uint32_t pre = (b1 << 11) | (uint32_t)res[0];
   const int r2 = r - res[1];
-  const int ntot = off[nc];
-  const uint2 *cand_q = a.ws.cand + (int64_t)q * nchunks * TOPK_CHUNK;
-  const bool in_lds = ntot <= LIST_CAP;
-  __syncthreads();
-  zero_lds<FIN_THREADS>(h1, 1024);
-  if (in_lds) {
-#pragma unroll
-    for (int j = 0; j < LIST_CAP / FIN_THREADS; ++j) {
-      const int i = t + j * FIN_THREADS;
-      if (i < ntot) {
-        const int cc = locate(off, nc, i);
-        lst[i] = cand_q[(int64_t)cc * TOPK_CHUNK + (i - off[cc])];
+  const int nbound = (int)h[res[0]];  // candidates with key[31:10] == pre
+  const int per = (ntot + LONG_THREADS - 1) / LONG_THREADS;
+  const int lo = min(ntot, per * t), hi = min(ntot, lo + per);
+  int32_t *out = a.idx + (int64_t)q * k;
+  int tot;
+  if (in_lds && nbound <= WAVE) {
+    // Few candidates share the boundary prefix (the usual case): one
+    // wavefront ranks them by (key descending, position ascending) and marks
+    // the chosen r2 in place (key all ones) and the rest (key 0), so the
+    // output below is a single comparison against the prefix.
+    __shared__ int nb_cnt;
+    __shared__ int bidx[WAVE];
+    if (t == 0) nb_cnt = 0;
+    __syncthreads();
+    for (int i = t; i < ntot; i += LONG_THREADS)
+      if ((tl[i].x >> 10) == pre) bidx[atomicAdd(&nb_cnt, 1)] = i;
+    __syncthreads();
+    if (t < WAVE) {
+      const bool have = t < nbound;
+      const uint2 me = have ? tl[bidx[t]] : make_uint2(0u, 0u);
+      int rank = 0;
+      for (int j = 0; j < nbound; ++j) {
+        const uint2 o = tl[bidx[j]];
+        rank += (o.x > me.x || (o.x == me.x && o.y < me.y)) ? 1 : 0;
+      }
+      // every lane has read every boundary entry before any is overwritten
+      __builtin_amdgcn_wave_barrier();
+      if (have) tl[bidx[t]].x = rank < r2 ? 0xFFFFFFFFu : 0u;
+    }
+    __syncthreads();
+    // Output in position order: key[31:10] > pre (the marked boundary keys included).
+    int my_sel = 0;
+    for (int i = lo; i < hi; ++i) my_sel += ((tl[i].x >> 10) > pre) ? 1 : 0;
+    int pos = block_exclusive_scan<LONG_THREADS>(my_sel, sm, tot);
+    for (int i = lo; i < hi; ++i) {
+      const uint2 e = tl[i];
+      if ((e.x >> 10) > pre) {
+        if (pos < k) out[pos] = (int32_t)e.y;
+        ++pos;
       }
     }
-  }
-  __syncthreads();
-  auto get = [&](int i) {
-    if (in_lds) return lst[i];
-    const int cc = locate(off, nc, i);
-    return cand_q[(int64_t)cc * TOPK_CHUNK + (i - off[cc])];
-  };
-  // Digit 3 over the candidates with key[31:10] == pre; contiguous runs per thread.
-  const int per = (ntot + FIN_THREADS - 1) / FIN_THREADS;
-  const int lo = min(ntot, per * t), hi = min(ntot, lo + per);
-  for (int i = lo; i < hi; ++i) {
-    const uint32_t kk = get(i).x;
-    if ((kk >> 10) == pre) atomicAdd(&h1[kk & 1023u], 1u);
-  }
-  __syncthreads();
-  find_rank_bin<FIN_THREADS, 1024>(h1, r2, sm, res);
-  const uint32_t kth = (pre << 10) | (uint32_t)res[0];
-  const int ties = r2 - res[1];
-  // Emission in position order.
-  int my_ties = 0;
-  for (int i = lo; i < hi; ++i) my_ties += (get(i).x == kth) ? 1 : 0;
-  int tot;
-  const int tie_rank = block_exclusive_scan<FIN_THREADS>(my_ties, sm, tot);
-  int my_sel = 0;
-  for (int i = lo, tr = tie_rank; i < hi; ++i) {
-    const uint32_t kk = get(i).x;
-    if (kk > kth || (kk == kth && tr < ties)) ++my_sel;
-    tr += (kk == kth) ? 1 : 0;
-  }
-  int pos = block_exclusive_scan<FIN_THREADS>(my_sel, sm, tot);
-  int32_t *out = a.idx + (int64_t)q * k;
-  for (int i = lo, tr = tie_rank; i < hi; ++i) {
-    const uint2 e = get(i);
-    if (e.x > kth || (e.x == kth && tr < ties)) {
-      if (pos < k) out[pos] = (int32_t)e.y;
-      ++pos;
+  } else {
+    __syncthreads();
+    zero_lds<LONG_THREADS>(h, 1024);
+    __syncthreads();
+    // Digit 3 over the candidates with key[31:10] == pre; contiguous runs per thread.
+    for (int i = lo; i < hi; ++i) {
+      const uint32_t kk = get(i).x;
+      if ((kk >> 10) == pre) atomicAdd(&h[kk & 1023u], 1u);
     }
-    tr += (e.x == kth) ? 1 : 0;
+    __syncthreads();
+    find_rank_bin<LONG_THREADS, 1024>(h, r2, sm, res);
+    const uint32_t kth = (pre << 10) | (uint32_t)res[0];
+    const int ties = r2 - res[1];
+    // Output in position order: keys > kth and the first `ties` keys == kth.
+    int my_ties = 0;
+    for (int i = lo; i < hi; ++i) my_ties += (get(i).x == kth) ? 1 : 0;
+    const int tie_rank = block_exclusive_scan<LONG_THREADS>(my_ties, sm, tot);
+    int my_sel = 0;
+    for (int i = lo, tr = tie_rank; i < hi; ++i) {
+      const uint32_t kk = get(i).x;
+      if (kk > kth || (kk == kth && tr < ties)) ++my_sel;
+      tr += (kk == kth) ? 1 : 0;
+    }
+    int pos = block_exclusive_scan<LONG_THREADS>(my_sel, sm, tot);
+    for (int i = lo, tr = tie_rank; i < hi; ++i) {
+      const uint2 e = get(i);
+      if (e.x > kth || (e.x == kth && tr < ties)) {
+        if (pos < k) out[pos] = (int32_t)e.y;
+        ++pos;
+      }
+      tr += (e.x == kth) ? 1 : 0;
+    }
   }
-  for (int i = tot + t; i < k; i += FIN_THREADS) out[i] = -1;  // defensive: tot == k
+  for (int i = tot + t; i < k; i += LONG_THREADS) out[i] = -1;  // defensive: tot == k
   if (t == 0 && a.count) a.count[q] = min(tot, k);
 }
 
 hipError_t launch_topk_init(const TopkWs &ws, int num_q, hipStream_t st) {
-  const int64_t n = (int64_t)num_q * (2 * TOPK_BINS + 1);
+  const int64_t n = (int64_t)num_q * TOPK_BINS;
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(topk_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, ws.hist, n);
   return hipGetLastError();
@@ -532,12 +593,12 @@ hipError_t launch_topk_select(const float *scores, int64_t ld, const int32_t *q_
   SelectArgs a{scores, ld, q_nvis, k, hist1_valid ? 1 : 0, idx, count, ws};
   hipLaunchKernelGGL(topk_row_kernel, dim3((unsigned)num_q), dim3(TK_THREADS), 0, st, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || ws.nchunks == 0 || max_nvis <= TOPK_ROW_MAX) return e;
-  const int64_t blocks = (int64_t)num_q * ws.nchunks;
-  hipLaunchKernelGGL(topk_chunk_kernel, dim3((unsigned)blocks), dim3(TK_THREADS), 0, st, a);
+  if (e != hipSuccess || ws.nblk == 0 || max_nvis <= TOPK_ROW_MAX) return e;
+  const int64_t blocks = (int64_t)num_q * ws.nblk;
+  hipLaunchKernelGGL(topk_long_kernel, dim3((unsigned)blocks), dim3(LONG_THREADS), 0, st, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_final_kernel, dim3((unsigned)num_q), dim3(FIN_THREADS), 0, st, a);
+  hipLaunchKernelGGL(topk_finish_kernel, dim3((unsigned)num_q), dim3(LONG_THREADS), 0, st, a);
   return hipGetLastError();
 }
 

@@ -99,3 +99,17 @@ def test_deterministic_repeat():
     a, ca = gpu_topk(rows, [50000] * 4, 2048)
     b, cb = gpu_topk(rows, [50000] * 4, 2048)
     assert (a == b).all() and (ca == cb).all()
+
+
+def test_long_row_boundaries():
+    """Just above the one-block row limit, a ragged span, and the longest
+    history the library accepts (2^20), once with distinct values and once
+    all equal (every position is a candidate; ties go to the lowest)."""
+    banner("topk long-row boundaries")
+    rng = np.random.default_rng(91)
+    nvis = [16385, 24577, 1 << 20, 1 << 20]
+    rows = [rng.standard_normal(16385).astype(np.float32),
+            np.round(rng.standard_normal(24577) * 2).astype(np.float32),
+            rng.standard_normal(1 << 20).astype(np.float32),
+            np.full(1 << 20, 0.25, np.float32)]
+    assert_same(rows, nvis, 2048, "long boundaries")
