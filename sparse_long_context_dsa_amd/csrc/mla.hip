@@ -191,8 +191,18 @@ __device__ __forceinline__ float xhalf_sum(float v) {
 template <bool WIDE>
 __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
   const MlaLaunch &a = p.a;
-  const int q = blockIdx.x / p.nsplit;
-  const int sp = blockIdx.x - q * p.nsplit;
+  // Decode splits: the blocks of one query run on one XCD (block b runs on
+  // XCD b % 8), so the query's q and partial outputs stay in that XCD's L2.
+  int q, sp;
+  if (p.nsplit == 1) {
+    q = blockIdx.x;
+    sp = 0;
+  } else {
+    const int y = blockIdx.x >> 3;
+    q = (y / p.nsplit) * 8 + (blockIdx.x & 7);
+    sp = y % p.nsplit;
+    if (q >= a.num_q) return;
+  }
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave-uniform
   const int g = lane >> 5, c = lane & 31;
@@ -524,10 +534,13 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
 
 // Merge split partials: out = sum_s exp(lse_s - M) O_s / sum_s exp(lse_s - M).
 __global__ __launch_bounds__(256) void mla_combine_kernel(const float *__restrict__ part_o,
-                                                          const float *__restrict__ part_lse, int nsplit,
+                                                          const float *__restrict__ part_lse, int nsplit, int num_q,
                                                           float *__restrict__ out, float *__restrict__ lse) {
-  const int q = blockIdx.x >> 6;
-  const int head = 2 * (blockIdx.x & 63) + (threadIdx.x >> 7);
+  // Same XCD as the query's split blocks (block b runs on XCD b % 8).
+  const int y = blockIdx.x >> 3;
+  const int q = (y >> 6) * 8 + (blockIdx.x & 7);
+  if (q >= num_q) return;
+  const int head = 2 * (y & 63) + (threadIdx.x >> 7);
   const int d = 4 * (threadIdx.x & 127);
   const float *pl = part_lse + (int64_t)q * nsplit * 128 + head;
   float mx = -INFINITY;
@@ -585,15 +598,16 @@ hipError_t launch_mla(const MlaLaunch &a, bool decode, void *ws, hipStream_t st)
   }
   // Offsets from the descriptor base stay below 4 GiB unless a paged pool is that large.
   const bool wide = a.map.block_shift >= 0 && a.num_rows * (int64_t)ROW_BYTES >= 0xFFFFF000ll - ROW_BYTES;
-  const dim3 grid((unsigned)((int64_t)a.num_q * p.nsplit));
+  const int64_t nq8 = (a.num_q + 7) / 8 * 8;  // split blocks are grouped by XCD
+  const dim3 grid((unsigned)(p.nsplit == 1 ? (int64_t)a.num_q : nq8 * p.nsplit));
   if (wide)
     hipLaunchKernelGGL(mla_kernel<true>, grid, dim3(MLA_THREADS), 0, st, p);
   else
     hipLaunchKernelGGL(mla_kernel<false>, grid, dim3(MLA_THREADS), 0, st, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.nsplit == 1) return e;
-  hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)((int64_t)a.num_q * 64)), dim3(256), 0, st, p.part_o,
-                     p.part_lse, p.nsplit, a.out, a.lse);
+  hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)(nq8 * 64)), dim3(256), 0, st, p.part_o, p.part_lse,
+                     p.nsplit, a.num_q, a.out, a.lse);
   return hipGetLastError();
 }
 
