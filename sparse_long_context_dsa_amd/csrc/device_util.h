@@ -22,6 +22,13 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Value of v in lane l (l uniform across the wavefront).
+__device__ __forceinline__ int64_t readlane64(int64_t v, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)v >> 32), l);
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // Order-preserving map fp32 -> uint32: a larger float gives a larger key.
 // -0 is mapped like +0 so that the two compare equal.
 __device__ __forceinline__ uint32_t order_key(float f) {

@@ -16,7 +16,10 @@
 // 8 KiB of FP8 q stays in registers for the whole run; keys stream from HBM
 // straight into the B-operand registers (each lane reads 32 contiguous bytes
 // of a key row; the two 64-byte halves of a row go to lane groups 0/1 and
-// 2/3), prefetched one step ahead.  ReLU, the weighting and 16 of the 64 head
+// 2/3), prefetched one step ahead into the other of two register buffers.
+// Every lane issues the same loads on every step (rows past the visible range
+// are clamped, not skipped), and the block-table lookups are done once before
+// the loop, so the waits on the prefetch count exactly the loads they need.  ReLU, the weighting and 16 of the 64 head
 // terms are summed in-lane; the remaining 4-way sum across lane groups is a
 // butterfly that also transposes, so lane l ends with the score of key s0+l.
 // Scores of four steps are staged in LDS and leave as 16-byte stores (1 KiB
@@ -53,21 +56,24 @@ struct KeyStep {
   float ks;
 };
 
-// Loads the B operands (4 tiles of 16 keys) of the 64-key step at s0.
-__device__ __forceinline__ void load_step(const IndexerLaunch &a, int seq, int s0, int nvis, int lane,
+// Loads the B operands (4 tiles of 16 keys) of the 64-key step at s0, whose
+// keys sit in the physical rows base .. base + 63.  Keys at or past nvis read
+// the step's last visible row instead: every lane always issues the same
+// loads (no branch, so the compiler's wait counts stay exact), and the scores
+// of those keys are never stored.
+__device__ __forceinline__ void load_step(const IndexerLaunch &a, int64_t base, int s0, int nvis, int lane,
                                           KeyStep &st) {
-  const int64_t base = phys_row(a.map, seq, s0);  // 64 | block size: the step is contiguous
   const int sub = lane & 15, half = lane >> 4;
+  const int last = nvis - 1 - s0;  // >= 0
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int key = s0 + 16 * t + sub;
-    if (key < nvis) {
-      st.b[t] = load32(a.k8 + (base + 16 * t + sub) * 128 + 32 * half);
-    } else {
-      st.b[t] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
-    }
-  }
-  st.ks = (s0 + lane < nvis) ? a.k_scale[base + lane] : 0.0f;
+  for (int t = 0; t < 4; ++t) st.b[t] = load32(a.k8 + (base + min(16 * t + sub, last)) * 128 + 32 * half);
+  st.ks = a.k_scale[base + min(lane, last)];
+}
+
+__device__ __forceinline__ float relu(float x) {
+  float r;
+  asm("v_max_f32 %0, 0, %1" : "=v"(r) : "v"(x));  // one instruction, no canonicalize
+  return r;
 }
 
 template <bool HIST>
@@ -76,7 +82,7 @@ __global__ __launch_bounds__(256) void indexer_kernel(IndexerLaunch a, int nchun
   const int chunk = blockIdx.x - q * nchunks;
   const int nvis = a.q_nvis[q];
   if (nvis <= a.skip_le || chunk * IDX_KPB >= nvis) return;  // block-uniform
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int seq = a.q_seq[q];
 
   __shared__ uint32_t hist[HIST ? TOPK_BINS : 1];
@@ -113,10 +119,44 @@ __global__ __launch_bounds__(256) void indexer_kernel(IndexerLaunch a, int nchun
   const int g = lane >> 4;
   const bool b1 = (g & 2) != 0, b0 = (g & 1) != 0;
 
-  KeyStep cur, nxt;
-  if (s_begin < s_end) load_step(a, seq, s_begin, nvis, lane, cur);
-  for (int s0 = s_begin; s0 < s_end; s0 += 64) {
-    if (s0 + 64 < s_end) load_step(a, seq, s0 + 64, nvis, lane, nxt);
+  // Physical row of each 64-key step of this wavefront's run (a step never
+  // straddles a cache block), one step per lane, looked up once: the loop then
+  // issues its key loads without waiting on a block-table read.
+  int64_t lane_row = 0;
+  if (s_begin + 64 * lane < s_end) lane_row = phys_row(a.map, seq, s_begin + 64 * lane);
+
+  // A finished group of 256 scores is stored one step late, after the next
+  // step's key loads are issued, so that the wait for those loads (vector
+  // memory completes in order) does not also wait on the store.
+  auto flush = [&](int g0) {
+    const float4 v = *reinterpret_cast<const float4 *>(&sbuf[wave][4 * lane]);
+    const int p0 = g0 + 4 * lane;
+    if (p0 + 3 < s_end) {
+      *reinterpret_cast<float4 *>(srow + p0) = v;
+    } else {
+      const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (p0 + e < s_end) srow[p0 + e] = vv[e];
+    }
+    if (HIST) {
+      const float vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (p0 + e < s_end) atomicAdd(&hist[order_key(vv[e]) >> 21], 1u);
+    }
+  };
+
+  int pending = -1;  // start of a group waiting to be stored
+  // One 64-key step: prefetch the next step into `nxt`, store a finished
+  // group, score the keys in `cur`.  The loop alternates two buffers, so no
+  // register copy forces an early wait on the prefetch.
+  auto step = [&](int s0, const KeyStep &cur, KeyStep *nxt) {
+    if (nxt) load_step(a, readlane64(lane_row, ((s0 - s_begin) >> 6) + 1), s0 + 64, nvis, lane, *nxt);
+    if (pending >= 0) {
+      flush(pending);
+      pending = -1;
+    }
     float p[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -125,7 +165,7 @@ __global__ __launch_bounds__(256) void indexer_kernel(IndexerLaunch a, int nchun
       for (int mt = 0; mt < 4; ++mt) {
         const v4f c = mfma_fp8_16x16x128(A[mt], cur.b[t], v4f{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc_sum = fmaf(coef[mt][r], fmaxf(c[r], 0.0f), acc_sum);
+        for (int r = 0; r < 4; ++r) acc_sum = fmaf(coef[mt][r], relu(c[r]), acc_sum);
       }
       p[t] = acc_sum;
     }
@@ -138,28 +178,27 @@ __global__ __launch_bounds__(256) void indexer_kernel(IndexerLaunch a, int nchun
     const float score = ((b0 ? x1 : x0) + rc) * cur.ks;
     const int j = ((s0 - s_begin) >> 6) & 3;  // step within the 256-key group
     sbuf[wave][64 * j + lane] = score;
-    if (j == 3 || s0 + 64 >= s_end) {
-      // Flush the group: lane l writes keys g0 + 4l .. g0 + 4l + 3.
-      const int g0 = s0 - 64 * j;
-      const float4 v = *reinterpret_cast<const float4 *>(&sbuf[wave][4 * lane]);
-      const int p0 = g0 + 4 * lane;
-      if (p0 + 3 < s_end) {
-        *reinterpret_cast<float4 *>(srow + p0) = v;
-      } else {
-        const float vv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (p0 + e < s_end) srow[p0 + e] = vv[e];
-      }
-      if (HIST) {
-        const float vv[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (p0 + e < s_end) atomicAdd(&hist[order_key(vv[e]) >> 21], 1u);
-      }
-    }
-    cur = nxt;
+    // Lane l stores keys g0 + 4l .. g0 + 4l + 3 of the group.
+    if (j == 3 || s0 + 64 >= s_end) pending = s0 - 64 * j;
+  };
+
+  // Steps are taken in pairs while both have a successor to prefetch; the
+  // last one or two are peeled, so the prefetch in the loop is unconditional.
+  const int nsteps = s_begin < s_end ? (s_end - s_begin + 63) >> 6 : 0;
+  KeyStep kb0, kb1;
+  if (nsteps > 0) load_step(a, readlane64(lane_row, 0), s_begin, nvis, lane, kb0);
+  int i = 0;
+  for (; i + 2 < nsteps; i += 2) {
+    step(s_begin + 64 * i, kb0, &kb1);
+    step(s_begin + 64 * (i + 1), kb1, &kb0);
   }
+  if (nsteps - i == 2) {
+    step(s_begin + 64 * i, kb0, &kb1);
+    step(s_begin + 64 * (i + 1), kb1, nullptr);
+  } else if (nsteps - i == 1) {
+    step(s_begin + 64 * i, kb0, nullptr);
+  }
+  if (pending >= 0) flush(pending);
 
   if (HIST) {
     __syncthreads();
