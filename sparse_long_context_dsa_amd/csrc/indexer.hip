@@ -9,7 +9,7 @@
 // scale is applied after the head sum, which is exact reordering because
 // k_scale > 0 and ReLU is positively homogeneous.
 //
-// Mapping: one wavefront owns one query and a run of IDX_KPW keys.  The 64
+// Mapping: one wavefront owns one query and a run of kpw keys.  The 64
 // indexer heads are the M side of v_mfma_scale_f32_16x16x128_f8f6f4 (4 M-tiles
 // of 16 heads, K = 128 = the whole head width, so one MFMA per 16x16 tile);
 // keys are the N side, 16 per tile, 4 tiles (64 keys) per step.  The query's
@@ -34,8 +34,9 @@
 namespace dsa {
 
 constexpr int IDX_WAVES = 4;
-constexpr int IDX_KPW = 512;                     // keys per wavefront (multiple of 256)
-constexpr int IDX_KPB = IDX_WAVES * IDX_KPW;     // keys per block
+constexpr int IDX_KPW_MIN = 256;                 // keys per wavefront: a multiple of 64,
+constexpr int IDX_KPW_MAX = 64 * WAVE;           // at most one 64-key step per lane
+constexpr int64_t IDX_MIN_WAVES = 32768;         // 32 wavefronts per SIMD
 
 __device__ __forceinline__ v4f mfma_fp8_16x16x128(const v8i &a, const v8i &b, const v4f &c) {
   // Format 0 = FP8 E4M3 for both operands; E8M0 scale 127 = 2^0 (no scaling).
@@ -77,11 +78,11 @@ __device__ __forceinline__ float relu(float x) {
 }
 
 template <bool HIST>
-__global__ __launch_bounds__(256) void indexer_kernel(IndexerLaunch a, int nchunks) {
+__global__ __launch_bounds__(256) void indexer_kernel(IndexerLaunch a, int nchunks, int kpw) {
   const int q = blockIdx.x / nchunks;
   const int chunk = blockIdx.x - q * nchunks;
   const int nvis = a.q_nvis[q];
-  if (nvis <= a.skip_le || chunk * IDX_KPB >= nvis) return;  // block-uniform
+  if (nvis <= a.skip_le || chunk * IDX_WAVES * kpw >= nvis) return;  // block-uniform
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int seq = a.q_seq[q];
 
@@ -113,8 +114,8 @@ __global__ __launch_bounds__(256) void indexer_kernel(IndexerLaunch a, int nchun
       coef[mt][r] = a.w[(int64_t)q * 64 + h] * qs;
     }
 
-  const int s_begin = chunk * IDX_KPB + wave * IDX_KPW;
-  const int s_end = min(s_begin + IDX_KPW, nvis);
+  const int s_begin = (chunk * IDX_WAVES + wave) * kpw;
+  const int s_end = min(s_begin + kpw, nvis);
   float *srow = a.scores + (int64_t)q * a.ld;
   const int g = lane >> 4;
   const bool b1 = (g & 2) != 0, b0 = (g & 1) != 0;
@@ -212,14 +213,24 @@ __global__ __launch_bounds__(256) void indexer_kernel(IndexerLaunch a, int nchun
 
 hipError_t launch_indexer(const IndexerLaunch &a, hipStream_t st) {
   if (a.num_q == 0 || a.max_nvis == 0) return hipSuccess;
-  const int nchunks = (a.max_nvis + IDX_KPB - 1) / IDX_KPB;
+  // The longest run per wavefront that still gives the chip enough
+  // wavefronts: long runs amortise each wavefront's set-up (its query's q,
+  // weights and histogram), short ones keep enough loads in flight when only
+  // a few queries stream long histories from HBM.
+  int kpw = IDX_KPW_MIN;
+  while (kpw < IDX_KPW_MAX) {
+    const int64_t chunks = (a.max_nvis + IDX_WAVES * 2 * kpw - 1) / (IDX_WAVES * 2 * kpw);
+    if ((int64_t)a.num_q * chunks * IDX_WAVES < IDX_MIN_WAVES) break;
+    kpw *= 2;
+  }
+  const int nchunks = (a.max_nvis + IDX_WAVES * kpw - 1) / (IDX_WAVES * kpw);
   const int64_t blocks = (int64_t)a.num_q * nchunks;
   if (a.hist)
     hipLaunchKernelGGL(indexer_kernel<true>, dim3((unsigned)blocks), dim3(IDX_WAVES * WAVE), 0, st, a,
-                       nchunks);
+                       nchunks, kpw);
   else
     hipLaunchKernelGGL(indexer_kernel<false>, dim3((unsigned)blocks), dim3(IDX_WAVES * WAVE), 0, st, a,
-                       nchunks);
+                       nchunks, kpw);
   return hipGetLastError();
 }
 
