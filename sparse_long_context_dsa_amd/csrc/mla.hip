@@ -235,12 +235,25 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
   // the contract; it is loaded from position 0 (in bounds, finite) and masked.
   const int seq = a.q_seq[q];
   const int32_t *ip = a.idx + (int64_t)q * a.k + r0;
+  // All of a thread's positions are loaded before any is used, so the loads
+  // (and the block-table reads that depend on them) overlap instead of
+  // taking one memory latency per row.
+  constexpr int PER_THREAD = MLA_MAX_ROWS / MLA_THREADS;
+  int pos[PER_THREAD];
+#pragma unroll
+  for (int j = 0; j < PER_THREAD; ++j) {
+    const int i = tid + j * MLA_THREADS;
+    pos[j] = i < nrows ? ip[i] : 0;
+  }
   int bad = 0;
-  for (int i = tid; i < nrows; i += MLA_THREADS) {
-    const int pos = ip[i];
-    const bool ok = pos >= 0 && pos < nvis;
-    prow[i] = (uint32_t)phys_row(a.map, seq, ok ? pos : 0) | (ok ? 0u : INVALID_ROW);
-    bad |= ok ? 0 : 1;
+#pragma unroll
+  for (int j = 0; j < PER_THREAD; ++j) {
+    const int i = tid + j * MLA_THREADS;
+    const bool ok = pos[j] >= 0 && pos[j] < nvis;
+    if (i < nrows) {
+      prow[i] = (uint32_t)phys_row(a.map, seq, ok ? pos[j] : 0) | (ok ? 0u : INVALID_ROW);
+      bad |= ok ? 0 : 1;
+    }
   }
   // The rest of the last tile repeats the last row (finite data, masked out of
   // the softmax), so the gathers need no clamping.
