@@ -100,6 +100,17 @@ __device__ __forceinline__ void scale_acc(float &x, float s) {
       : "v"(s));
 }
 
+// One accumulator register times s, as a VGPR value (the AGPR is unchanged).
+__device__ __forceinline__ float read_scaled(const float &x, float s) {
+  float r;
+  asm("v_accvgpr_read_b32 %0, %1\n\t"
+      "s_nop 1\n\t"
+      "v_mul_f32 %0, %0, %2"
+      : "=&v"(r)
+      : "a"(x), "v"(s));
+  return r;
+}
+
 // S^T chain of the QK product on a VGPR accumulator.  Written as asm
 // statements so that S stays in VGPRs (next to the softmax that reads it)
 // while all 256 AGPRs hold O; register operands only, and not volatile, so
@@ -264,14 +275,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
     prow[nrows + tid] = (uint32_t)phys_row(a.map, seq, ok ? pos : 0) | (ok ? 0u : INVALID_ROW);
   }
 
-  // Queries of this wavefront's own 32 heads: B fragments of S^T = K . Q^T.
   const int head = 32 * wave + c;
-  uint4 qb[36];
-  {
-    const uint16_t *qr = a.q + ((int64_t)q * 128 + head) * 576 + 8 * g;
-#pragma unroll
-    for (int ks = 0; ks < 36; ++ks) qb[ks] = *reinterpret_cast<const uint4 *>(qr + 16 * ks);
-  }
 
   // O[mt][nt]: M-tile 0 = own heads, 1 = partner heads; N-tile nt = value
   // dims 256*dh + 32*nt .. +31.
@@ -315,6 +319,14 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
       const_cast<uint16_t *>(a.kv + (size_t)brow * 576), (short)0, 0xFFFFFFFF, 0x00020000);
   if (ntiles > 0) issue_tile<WIDE>(rs, a.kv, brow, prow, 0, true, tb0, wave, lane);
   if (ntiles > 1) issue_tile<WIDE>(rs, a.kv, brow, prow, MLA_T, true, tb1, wave, lane);
+  // Queries of this wavefront's own 32 heads: B fragments of S^T = K . Q^T,
+  // loaded while the first two tiles are gathered.
+  uint4 qb[36];
+  {
+    const uint16_t *qr = a.q + ((int64_t)q * 128 + head) * 576 + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < 36; ++ks) qb[ks] = *reinterpret_cast<const uint4 *>(qr + 16 * ks);
+  }
 
   // One tile: wait for it, start the gather of tile t + 2 into nbuf, compute.
   auto tile_step = [&](const int t, const uint8_t *buf, uint8_t *nbuf) {
@@ -506,19 +518,6 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
   const float lse_v = (l_tot > 0.0f) ? m_ref * LN2 + logf(l_tot) : -INFINITY;
   if (g == 0) aex[wave][c] = inv;
   __syncthreads();
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-    float il[16];
-    read_head_values(aex[mt == 0 ? wave : partner], g, il);
-#pragma unroll
-    for (int nt = 0; nt < 8; ++nt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float x = o[mt][nt][i];
-        scale_acc(x, il[i]);
-        o[mt][nt][i] = x;
-      }
-  }
 
   float *obase;
   float *lbase;
@@ -529,9 +528,12 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
     obase = p.part_o + ((int64_t)q * p.nsplit + sp) * 128 * 512;
     lbase = p.part_lse + ((int64_t)q * p.nsplit + sp) * 128;
   }
+  // Each value is scaled by its head's 1/l on its way out of the AGPRs.
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
     const int hset = 32 * (mt == 0 ? wave : partner);
+    float il[16];
+    read_head_values(aex[mt == 0 ? wave : partner], g, il);
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
@@ -539,7 +541,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int h = hset + 8 * i + 4 * g + j;
-          obase[(int64_t)h * 512 + 256 * dh + 32 * nt + c] = o[mt][nt][4 * i + j];
+          obase[(int64_t)h * 512 + 256 * dh + 32 * nt + c] = read_scaled(o[mt][nt][4 * i + j], il[4 * i + j]);
         }
   }
   if (lbase && g == 0) lbase[head] = lse_v;
