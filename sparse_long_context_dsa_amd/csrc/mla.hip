@@ -33,6 +33,8 @@
 // Decode splits a query's rows over several blocks that write (O/l, lse)
 // partials; mla_combine_kernel merges them.  Prefill gives each query one
 // block and writes the result directly.
+#include <type_traits>
+
 #include "device_util.h"
 #include "dsa_internal.h"
 
@@ -158,25 +160,35 @@ __device__ __forceinline__ void read_head_values(const float *x, int g, float *v
 // counts.  A paged pool of 4 GiB or more (WIDE) takes the global form with
 // 64-bit per-lane addresses, which the compiler treats as touching LDS and
 // memory both: its LDS reads then wait for all LDS traffic.
+//
+// tile_row gives the lane's source row; issue_part issues part i of the
+// gather (so that a caller can spread the parts between other work).
+// Rows of a partial last tile past `last` repeat row `last` (finite data,
+// masked out of the softmax).
+__device__ __forceinline__ uint32_t tile_row(const uint32_t *prow, int r0, bool real, int last, int wave,
+                                             int lane) {
+  return prow[real ? min(r0 + 8 * wave + (lane >> 3), last) : 0] & ~INVALID_ROW;
+}
+template <bool WIDE>
+__device__ __forceinline__ void issue_part(const __amdgpu_buffer_rsrc_t rs, const uint16_t *__restrict__ kv,
+                                           uint32_t brow, uint32_t row, uint8_t *buf, int wave, int lane, int i) {
+  const int cx = (lane & 7) ^ (lane >> 3) ^ (wave & 1);
+  uint8_t *dst = buf + 9216 * wave + 1024 * i;
+  if (WIDE) {
+    const uint16_t *src = kv + (size_t)row * 576 + 8 * cx + 64 * i;
+    __builtin_amdgcn_global_load_lds(src, (lds_void *)dst, 16, 0, 0);
+  } else {
+    const uint32_t voff = (row - brow) * ROW_BYTES + 16 * cx + 128 * i;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dst, 16, voff, 0, 0, 0);
+  }
+}
 template <bool WIDE>
 __device__ __forceinline__ void issue_tile(const __amdgpu_buffer_rsrc_t rs, const uint16_t *__restrict__ kv,
-                                           uint32_t brow, const uint32_t *prow, int r0, bool real, uint8_t *buf,
-                                           int wave, int lane) {
-  const int rl = lane >> 3;
-  const uint32_t row = prow[real ? r0 + 8 * wave + rl : 0] & ~INVALID_ROW;
-  const int cx = (lane & 7) ^ rl ^ (wave & 1);
-  uint8_t *dst = buf + 9216 * wave;
-  if (WIDE) {
-    const uint16_t *src = kv + (size_t)row * 576 + 8 * cx;
+                                           uint32_t brow, const uint32_t *prow, int r0, bool real, int last,
+                                           uint8_t *buf, int wave, int lane) {
+  const uint32_t row = tile_row(prow, r0, real, last, wave, lane);
 #pragma unroll
-    for (int i = 0; i < LOADS_PER_WAVE; ++i)
-      __builtin_amdgcn_global_load_lds(src + 64 * i, (lds_void *)(dst + 1024 * i), 16, 0, 0);
-  } else {
-    const uint32_t voff = (row - brow) * ROW_BYTES + 16 * cx;
-#pragma unroll
-    for (int i = 0; i < LOADS_PER_WAVE; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)(dst + 1024 * i), 16, voff + 128 * i, 0, 0, 0);
-  }
+  for (int i = 0; i < LOADS_PER_WAVE; ++i) issue_part<WIDE>(rs, kv, brow, row, buf, wave, lane, i);
 }
 
 // max(a, b, c) in one instruction.  fmaxf would add a canonicalising
@@ -199,7 +211,7 @@ __device__ __forceinline__ float xhalf_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <bool WIDE>
+template <bool WIDE, bool PIPE>
 __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
   const MlaLaunch &a = p.a;
   // Decode splits: the blocks of one query run on one XCD (block b runs on
@@ -226,15 +238,19 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t tb0[TILE_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t tb1[TILE_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t tb2[TILE_BYTES];
+  // Physical row per selected position (bit 31: outside [0, n_vis)); the
+  // tail keeps the masked reads of a partial last tile in bounds.
   __shared__ __attribute__((aligned(16))) uint32_t prow[MLA_MAX_ROWS + MLA_T];
   // Per-tile exchange within a wavefront pair: P of the sender's 32 heads as
   // bf16 A fragments (lane-major, 2 x 16 bytes per lane), the rescale flag
-  // and factors.  One slot per wavefront suffices: the partner's reads of
-  // tile t complete (their MFMAs consume them) before it reaches the barrier
-  // that precedes the sender's writes of tile t + 1.
-  __shared__ __attribute__((aligned(16))) uint4 pex[MLA_WAVES][2][WAVE];
-  __shared__ __attribute__((aligned(16))) float aex[MLA_WAVES][32];
-  __shared__ int fex[MLA_WAVES];
+  // and factors.  The in-order schedule uses slot 0 only: the partner's reads
+  // of tile t complete (their MFMAs consume them) before it reaches the
+  // barrier that precedes the sender's writes of tile t + 1.  The pipelined
+  // schedule consumes tile t's P one step later, so it alternates slots.
+  __shared__ __attribute__((aligned(16))) uint4 pex[2][MLA_WAVES][2][WAVE];
+  __shared__ __attribute__((aligned(16))) float aex[2][MLA_WAVES][32];
+  __shared__ int fex[2][MLA_WAVES];
+  __shared__ __attribute__((aligned(16))) float iex[MLA_WAVES][32];  // 1/l per head, for the epilogue
 
   const int nvis = a.q_nvis[q];
   int cnt = a.count ? a.count[q] : a.k;
@@ -246,33 +262,45 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
   // the contract; it is loaded from position 0 (in bounds, finite) and masked.
   const int seq = a.q_seq[q];
   const int32_t *ip = a.idx + (int64_t)q * a.k + r0;
-  // All of a thread's positions are loaded before any is used, so the loads
-  // (and the block-table reads that depend on them) overlap instead of
-  // taking one memory latency per row.
+  // All of a thread's positions, and then their block-table entries, are
+  // loaded before any is used, every lane issuing the same loads (indices
+  // clamped into range, no branch), so they overlap instead of taking one
+  // memory latency per row.
   constexpr int PER_THREAD = MLA_MAX_ROWS / MLA_THREADS;
-  int pos[PER_THREAD];
-#pragma unroll
-  for (int j = 0; j < PER_THREAD; ++j) {
-    const int i = tid + j * MLA_THREADS;
-    pos[j] = i < nrows ? ip[i] : 0;
-  }
   int bad = 0;
+  if (nrows > 0) {  // block-uniform
+    int pos[PER_THREAD];
 #pragma unroll
-  for (int j = 0; j < PER_THREAD; ++j) {
-    const int i = tid + j * MLA_THREADS;
-    const bool ok = pos[j] >= 0 && pos[j] < nvis;
-    if (i < nrows) {
-      prow[i] = (uint32_t)phys_row(a.map, seq, ok ? pos[j] : 0) | (ok ? 0u : INVALID_ROW);
-      bad |= ok ? 0 : 1;
+    for (int j = 0; j < PER_THREAD; ++j) pos[j] = ip[min(tid + j * MLA_THREADS, nrows - 1)];
+    bool ok[PER_THREAD];
+#pragma unroll
+    for (int j = 0; j < PER_THREAD; ++j) {
+      ok[j] = pos[j] >= 0 && pos[j] < nvis;
+      pos[j] = ok[j] ? pos[j] : 0;
     }
-  }
-  // The rest of the last tile repeats the last row (finite data, masked out of
-  // the softmax), so the gathers need no clamping.
-  const int nrows_pad = (nrows + MLA_T - 1) / MLA_T * MLA_T;
-  if (nrows > 0 && tid < nrows_pad - nrows) {
-    const int pos = ip[nrows - 1];
-    const bool ok = pos >= 0 && pos < nvis;
-    prow[nrows + tid] = (uint32_t)phys_row(a.map, seq, ok ? pos : 0) | (ok ? 0u : INVALID_ROW);
+    uint32_t row[PER_THREAD];
+    if (a.map.block_shift < 0) {  // contiguous
+      const uint32_t r0 = (uint32_t)a.map.seq_row0[seq];
+#pragma unroll
+      for (int j = 0; j < PER_THREAD; ++j) row[j] = r0 + (uint32_t)pos[j];
+    } else {  // paged
+      const int32_t *bt = a.map.block_table + (int64_t)seq * a.map.max_blocks;
+      const int sh = a.map.block_shift;
+      int32_t blk[PER_THREAD];
+#pragma unroll
+      for (int j = 0; j < PER_THREAD; ++j) blk[j] = bt[pos[j] >> sh];
+#pragma unroll
+      for (int j = 0; j < PER_THREAD; ++j)
+        row[j] = ((uint32_t)blk[j] << sh) + (uint32_t)(pos[j] & ((1 << sh) - 1));
+    }
+#pragma unroll
+    for (int j = 0; j < PER_THREAD; ++j) {
+      const int i = tid + j * MLA_THREADS;
+      if (i < nrows) {
+        prow[i] = row[j] | (ok[j] ? 0u : INVALID_ROW);
+        bad |= ok[j] ? 0 : 1;
+      }
+    }
   }
 
   const int head = 32 * wave + c;
@@ -317,8 +345,8 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
       (!WIDE && a.map.block_shift < 0) ? (uint32_t)a.map.seq_row0[seq] : 0u);
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t *>(a.kv + (size_t)brow * 576), (short)0, 0xFFFFFFFF, 0x00020000);
-  if (ntiles > 0) issue_tile<WIDE>(rs, a.kv, brow, prow, 0, true, tb0, wave, lane);
-  if (ntiles > 1) issue_tile<WIDE>(rs, a.kv, brow, prow, MLA_T, true, tb1, wave, lane);
+  if (ntiles > 0) issue_tile<WIDE>(rs, a.kv, brow, prow, 0, true, nrows - 1, tb0, wave, lane);
+  if (!PIPE && ntiles > 1) issue_tile<WIDE>(rs, a.kv, brow, prow, MLA_T, true, nrows - 1, tb1, wave, lane);
   // Queries of this wavefront's own 32 heads: B fragments of S^T = K . Q^T,
   // loaded while the first two tiles are gathered.
   uint4 qb[36];
@@ -328,33 +356,13 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
     for (int ks = 0; ks < 36; ++ks) qb[ks] = *reinterpret_cast<const uint4 *>(qr + 16 * ks);
   }
 
-  // One tile: wait for it, start the gather of tile t + 2 into nbuf, compute.
-  auto tile_step = [&](const int t, const uint8_t *buf, uint8_t *nbuf) {
-    // Tile t must have landed (every wave's part of it): wait for this
-    // wave's loads of tile t, then the barrier.  Tile t+1 may stay in flight.
-    // A bare s_barrier: __syncthreads() would add a workgroup release fence,
-    // which waits for every outstanding LDS DMA, tile t+1 included.  LDS
-    // reads of the previous tile have completed (their MFMAs consumed them).
-    if (t + 1 < ntiles)
-      __builtin_amdgcn_s_waitcnt(0xF70 | LOADS_PER_WAVE);  // vmcnt(9)
-    else
-      __builtin_amdgcn_s_waitcnt(0xF70);                   // vmcnt(0)
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    // The buffer of tile t-1 is free now (every wave is past its compute):
-    // tile t + 2 goes into it.  Past the last
-    // tile the parts still issue (no branch between the MFMAs, which would
-    // make the compiler drain the LDS read ring), but all read one row of
-    // this block, which stays in cache, into the free buffer.
-    const bool next2 = t + 2 < ntiles;
-    const int t0 = t * MLA_T;
-    issue_tile<WIDE>(rs, a.kv, brow, prow, t0 + 2 * MLA_T, next2, nbuf, wave, lane);
-    __builtin_amdgcn_sched_barrier(0);
+  // ---- One tile, in pieces shared by the two schedules below. ----
+  auto no_hook = [](int) {};
 
-    // S^T[row, head] for 32 rows x the 32 own heads.
-    // K fragments are read QK_AHEAD steps ahead of their MFMA (ring buffer).
-    v16f s;
+  // S^T[row, head] for the tile's 32 rows x the 32 own heads.  K fragments
+  // are read QK_AHEAD steps ahead of their MFMA (ring buffer); hook(ks) runs
+  // after the MFMA of step ks.
+  auto qk = [&](const uint8_t *buf, v16f &s, auto &&hook) {
     constexpr int QK_AHEAD = 4;
     uint4 kf[QK_AHEAD + 1];
 #pragma unroll
@@ -369,19 +377,21 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
         mfma_s_first(s, kf[0], qb[0]);
       else
         mfma_s(s, kf[ks % (QK_AHEAD + 1)], qb[ks]);
+      hook(ks);
       // Keep the written order: the scheduler would otherwise sink each read
       // next to its MFMA and undo the prefetch distance.
       __builtin_amdgcn_sched_barrier(0);
     }
     mfma_s_drain(s);
+  };
 
-    // Online softmax for own head c over this tile's rows 8i + 4g + j, in
-    // log2 units: z = scale_log2 * s, folded into the exp2 argument below
-    // (scale_log2 > 0, so the max of z is scale_log2 times the max of s).
-    // Only a partial last tile, or a block whose list holds positions outside
-    // [0, n_vis), masks rows to -inf.
-    float z[16];
-    float zscale, tmax;
+  // Online softmax for own head c over the tile's rows 8i + 4g + j, in log2
+  // units: z = scale_log2 * s, folded into the exp2 argument (zscale) when no
+  // row is masked (scale_log2 > 0, so the max of z is scale_log2 times the
+  // max of s).  Only a partial last tile, or a block whose list holds
+  // positions outside [0, n_vis), masks rows to -inf.  Returns the tile max.
+  auto tile_max = [&](const int t0, const v16f &s, float *z, float &zscale) -> float {
+    float tmax;
     if (!any_bad && t0 + MLA_T <= nrows) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) z[i] = s[i];
@@ -409,67 +419,36 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
       tmax = xhalf_max(tmax);
       zscale = 1.0f;
     }
-    // The reference max moves only when a head's tile max exceeds it by more
-    // than RESCALE_LOG2 (always on the first tile with a valid row), so P <=
-    // 2^RESCALE_LOG2 and O is rescaled rarely.  An all-masked tile changes nothing.
-    const bool resc = __ballot(tmax > m_ref + RESCALE_LOG2) != 0ull;
-    if (resc) {
-      const float m_new = fmaxf(m_ref, tmax);
-      const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);  // 0 while m_ref = -inf
+    return tmax;
+  };
+
+  // The softmax update of one tile in 10 pieces, so that the pipelined
+  // schedule can spread them between MFMAs.  Piece 0 moves the reference max
+  // only when a head's tile max exceeds it by more than RESCALE_LOG2 (always
+  // on the first tile with a valid row), so P <= 2^RESCALE_LOG2 and O is
+  // rescaled rarely; an all-masked tile changes nothing.  Pieces 1-8 turn
+  // two rows each into P (bf16 pairs) and the tile's sum, which piece 9 adds
+  // to l_run.
+  auto softmax_piece = [&](const int j, const float *z, const float zscale, const float tmax, bool &resc,
+                           float &alpha, float &nmref, float &psum, uint32_t *pk) {
+    if (j == 0) {
+      resc = __ballot(tmax > m_ref + RESCALE_LOG2) != 0ull;
+      const float m_new = resc ? fmaxf(m_ref, tmax) : m_ref;
+      alpha = resc ? __builtin_amdgcn_exp2f(m_ref - m_new) : 1.0f;  // 0 while m_ref = -inf
       l_run *= alpha;
       m_ref = m_new;
-      if (g == 0) aex[wave][c] = alpha;
-    }
-    if (lane == 0) fex[wave] = resc ? 1 : 0;
-    const float nmref = (m_ref == -INFINITY) ? 0.0f : -m_ref;  // all rows so far masked: z = -inf, p = 0
-    float ps[8];
-    uint32_t pk[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
+      nmref = (m_ref == -INFINITY) ? 0.0f : -m_ref;  // all rows so far masked: z = -inf, p = 0
+      psum = 0.0f;
+    } else if (j <= 8) {
+      const int i = j - 1;
       const float e0 = __builtin_amdgcn_exp2f(fmaf(z[2 * i], zscale, nmref));
       const float e1 = __builtin_amdgcn_exp2f(fmaf(z[2 * i + 1], zscale, nmref));
-      ps[i] = e0 + e1;
+      psum += e0 + e1;
       pk[i] = pack_bf16(e0, e1);
+    } else if (j == 9) {
+      l_run += psum;
     }
-    l_run += ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
-    const uint4 pa0 = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-    const uint4 pa1 = make_uint4(pk[4], pk[5], pk[6], pk[7]);
-    pex[wave][0][lane] = pa0;
-    pex[wave][1][lane] = pa1;
-
-    // Publish P and the rescale factors to the partner: LDS writes done, then
-    // the barrier (bare, so the DMA of tiles t+1 and t+2 stays in flight).
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    const uint4 pp0 = pex[partner][0][lane];
-    const uint4 pp1 = pex[partner][1][lane];
-    if (t > 0) {  // O is still zero on the first tile
-      float al[16];
-      if (resc) {
-        read_head_values(aex[wave], g, al);
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            float x = o[0][nt][i];
-            scale_acc(x, al[i]);
-            o[0][nt][i] = x;
-          }
-      }
-      if (fex[partner]) {
-        read_head_values(aex[partner], g, al);
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            float x = o[1][nt][i];
-            scale_acc(x, al[i]);
-            o[1][nt][i] = x;
-          }
-      }
-    }
+  };
 
     // O += P . V over the tile's 32 rows (2 k-steps of 16), for both head
     // sets of the pair; each V fragment feeds two MFMAs.  The k-slots of lane
@@ -478,8 +457,11 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
     // transposing read gives lane l the 4 rows of one of those sets at column
     // n = l % 32: lanes 4r..4r+3 of each 16-lane group point at row r of the
     // set, 4 columns each.  16 steps j = (ks2, nt); the B fragment of step j
-    // is read PV_AHEAD steps ahead of its MFMAs (ring buffer).
-    constexpr int PV_AHEAD = 4;
+    // is read PV_AHEAD steps ahead of its MFMAs (ring buffer).  hook(j) runs
+    // between the two MFMAs of step j.
+  auto pv = [&](const uint8_t *buf, const uint4 &a0, const uint4 &a1, const uint4 &b0, const uint4 &b1,
+                auto &&hook) {
+    constexpr int PV_AHEAD = PIPE ? 2 : 4;
     auto v_frag = [&](int j) {
       const int ks2 = j >> 3, nt = j & 7;
       const int off0 = tr_base[nt & 1][0] + 9216 * (2 * ks2) + 1024 * (nt >> 1);  // half 0
@@ -497,15 +479,155 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
       if (j + PV_AHEAD < 16) vf[(j + PV_AHEAD) % (PV_AHEAD + 1)] = v_frag(j + PV_AHEAD);
       const int nt = j & 7;
       const v8bf vb = as_bf(vf[j % (PV_AHEAD + 1)]);
-      o[0][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(j < 8 ? pa0 : pa1), vb, o[0][nt], 0, 0, 0);
-      o[1][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(j < 8 ? pp0 : pp1), vb, o[1][nt], 0, 0, 0);
+      o[0][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(j < 8 ? a0 : a1), vb, o[0][nt], 0, 0, 0);
+      hook(j);
+      o[1][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(j < 8 ? b0 : b1), vb, o[1][nt], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  for (int t = 0; t < ntiles; t += NBUF) {
-    tile_step(t, tb0, tb2);
-    if (t + 1 < ntiles) tile_step(t + 1, tb1, tb0);
-    if (t + 2 < ntiles) tile_step(t + 2, tb2, tb1);
+
+  // O rows of own heads (mt 0) or of the partner's (mt 1) times per-head factors.
+  auto rescale_o = [&](const int mt, const float *fac) {
+    float al[16];
+    read_head_values(fac, g, al);
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float x = o[mt][nt][i];
+        scale_acc(x, al[i]);
+        o[mt][nt][i] = x;
+      }
+  };
+
+  // Tile t must have landed (every wave's part of it): wait for this wave's
+  // loads of tile t, then the barrier.  In the in-order schedule tile t+1 is
+  // already in flight and may stay so; the pipelined one issues it later.  A
+  // bare s_barrier: __syncthreads() would add a workgroup release fence,
+  // which waits for every outstanding LDS DMA, tile t+1 included.
+  auto wait_tile = [&](const int t) {
+    if (!PIPE && t + 1 < ntiles)
+      __builtin_amdgcn_s_waitcnt(0xF70 | LOADS_PER_WAVE);  // vmcnt(9)
+    else
+      __builtin_amdgcn_s_waitcnt(0xF70);                   // vmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  // LDS writes done, then a bare barrier (the DMA of later tiles stays in flight).
+  auto publish = [&]() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
+  if (!PIPE) {
+    // In-order schedule (decode, where the gathers come from HBM): the
+    // gather of tile t + 2 starts as tile t's compute starts, two tiles
+    // ahead; then QK, softmax, exchange and PV of tile t.
+    auto tile_step = [&](const int t, const uint8_t *buf, uint8_t *nbuf) {
+      wait_tile(t);
+      // The buffer of tile t-1 is free now (every wave is past its compute):
+      // tile t + 2 goes into it.  Past the last tile the parts still issue
+      // (no branch between the MFMAs, which would make the compiler drain the
+      // LDS read ring), but all read one row of this block, which stays in
+      // cache, into the free buffer.
+      issue_tile<WIDE>(rs, a.kv, brow, prow, t * MLA_T + 2 * MLA_T, t + 2 < ntiles, nrows - 1, nbuf, wave, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      v16f s;
+      qk(buf, s, no_hook);
+      float z[16], zscale;
+      const float tmax = tile_max(t * MLA_T, s, z, zscale);
+      bool resc;
+      float alpha, nmref, psum;
+      uint32_t pk[8];
+#pragma unroll
+      for (int j = 0; j < 10; ++j) softmax_piece(j, z, zscale, tmax, resc, alpha, nmref, psum, pk);
+      if (resc && g == 0) aex[0][wave][c] = alpha;
+      if (lane == 0) fex[0][wave] = resc ? 1 : 0;
+      const uint4 pa0 = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+      const uint4 pa1 = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+      pex[0][wave][0][lane] = pa0;
+      pex[0][wave][1][lane] = pa1;
+      publish();
+      const uint4 pp0 = pex[0][partner][0][lane];
+      const uint4 pp1 = pex[0][partner][1][lane];
+      if (t > 0) {  // O is still zero on the first tile
+        if (resc) rescale_o(0, aex[0][wave]);
+        if (fex[0][partner]) rescale_o(1, aex[0][partner]);
+      }
+      pv(buf, pa0, pa1, pp0, pp1, no_hook);
+    };
+    for (int t = 0; t < ntiles; t += NBUF) {
+      tile_step(t, tb0, tb2);
+      if (t + 1 < ntiles) tile_step(t + 1, tb1, tb0);
+      if (t + 2 < ntiles) tile_step(t + 2, tb2, tb1);
+    }
+  } else {
+    // Pipelined schedule (prefill, where the gathers mostly hit the caches):
+    // tile t's QK, with the gather of tile t + 1 issued between its MFMAs;
+    // then tile t-1's PV with tile t's softmax spread between its MFMAs, so
+    // the matrix cores, the vector ALUs and the memory pipeline work at once.
+    // P of tile t is consumed one tile later, so the exchange slots
+    // alternate, and O is rescaled for tile t's reference max just before
+    // that PV (the partner's flag is read a whole QK earlier).
+    bool resc_prev = false;
+    int pflag_prev = 0;
+    // Tile t-1's buffer is free once the publishing barrier of tile t-1 has
+    // been passed; tile t + 1 goes into the buffer of tile t - 2.
+    auto tile_step = [&](const int t, const uint8_t *buf, uint8_t *nbuf, const uint8_t *pbuf, auto prev) {
+      constexpr bool PREV = decltype(prev)::value;
+      wait_tile(t);
+      // Past the last tile the parts read one cached row into the free buffer.
+      const uint32_t nrow = tile_row(prow, (t + 1) * MLA_T, t + 1 < ntiles, nrows - 1, wave, lane);
+      v16f s;
+      qk(buf, s, [&](const int ks) {
+        if (ks < LOADS_PER_WAVE) issue_part<WIDE>(rs, a.kv, brow, nrow, nbuf, wave, lane, ks);
+      });
+      float z[16], zscale;
+      const float tmax = tile_max(t * MLA_T, s, z, zscale);
+      bool resc;
+      float alpha, nmref, psum;
+      uint32_t pk[8];
+      if (PREV) {
+        const int ps = (t - 1) & 1;
+        if (resc_prev) rescale_o(0, aex[ps][wave]);
+        if (pflag_prev) rescale_o(1, aex[ps][partner]);
+        const uint4 qa0 = pex[ps][wave][0][lane], qa1 = pex[ps][wave][1][lane];
+        const uint4 qp0 = pex[ps][partner][0][lane], qp1 = pex[ps][partner][1][lane];
+        pv(pbuf, qa0, qa1, qp0, qp1, [&](const int j) {
+          if (j < 10) softmax_piece(j, z, zscale, tmax, resc, alpha, nmref, psum, pk);
+        });
+      } else {
+#pragma unroll
+        for (int j = 0; j < 10; ++j) softmax_piece(j, z, zscale, tmax, resc, alpha, nmref, psum, pk);
+      }
+      const int sl = t & 1;
+      if (g == 0) aex[sl][wave][c] = alpha;
+      if (lane == 0) fex[sl][wave] = resc ? 1 : 0;
+      pex[sl][wave][0][lane] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+      pex[sl][wave][1][lane] = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+      publish();
+      // O is still zero until tile 0's PV, which tile 0's factors precede.
+      resc_prev = PREV && resc;
+      pflag_prev = PREV ? fex[sl][partner] : 0;
+    };
+    using First = std::integral_constant<bool, false>;
+    using Later = std::integral_constant<bool, true>;
+    if (ntiles > 0) tile_step(0, tb0, tb1, tb2, First{});
+    for (int t = 1; t < ntiles; t += NBUF) {
+      tile_step(t, tb1, tb2, tb0, Later{});
+      if (t + 1 < ntiles) tile_step(t + 1, tb2, tb0, tb1, Later{});
+      if (t + 2 < ntiles) tile_step(t + 2, tb0, tb1, tb2, Later{});
+    }
+    if (ntiles > 0) {
+      const int lt = (ntiles - 1) % NBUF, ps = (ntiles - 1) & 1;
+      if (resc_prev) rescale_o(0, aex[ps][wave]);
+      if (pflag_prev) rescale_o(1, aex[ps][partner]);
+      const uint4 qa0 = pex[ps][wave][0][lane], qa1 = pex[ps][wave][1][lane];
+      const uint4 qp0 = pex[ps][partner][0][lane], qp1 = pex[ps][partner][1][lane];
+      pv(lt == 0 ? tb0 : lt == 1 ? tb1 : tb2, qa0, qa1, qp0, qp1, no_hook);
+    }
   }
   // The last two tiles issued gathers past the end: let them land before the
   // block's LDS can be handed to another block.
@@ -516,7 +638,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
   const float l_tot = xhalf_sum(l_run);
   const float inv = (l_tot > 0.0f) ? 1.0f / l_tot : 0.0f;
   const float lse_v = (l_tot > 0.0f) ? m_ref * LN2 + logf(l_tot) : -INFINITY;
-  if (g == 0) aex[wave][c] = inv;
+  if (g == 0) iex[wave][c] = inv;
   __syncthreads();
 
   float *obase;
@@ -533,7 +655,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
   for (int mt = 0; mt < 2; ++mt) {
     const int hset = 32 * (mt == 0 ? wave : partner);
     float il[16];
-    read_head_values(aex[mt == 0 ? wave : partner], g, il);
+    read_head_values(iex[mt == 0 ? wave : partner], g, il);
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
@@ -615,10 +737,19 @@ hipError_t launch_mla(const MlaLaunch &a, bool decode, void *ws, hipStream_t st)
   const bool wide = a.map.block_shift >= 0 && a.num_rows * (int64_t)ROW_BYTES >= 0xFFFFF000ll - ROW_BYTES;
   const int64_t nq8 = (a.num_q + 7) / 8 * 8;  // split blocks are grouped by XCD
   const dim3 grid((unsigned)(p.nsplit == 1 ? (int64_t)a.num_q : nq8 * p.nsplit));
-  if (wide)
-    hipLaunchKernelGGL(mla_kernel<true>, grid, dim3(MLA_THREADS), 0, st, p);
-  else
-    hipLaunchKernelGGL(mla_kernel<false>, grid, dim3(MLA_THREADS), 0, st, p);
+  // Without splits (prefill) the pipelined schedule; with them (decode) the
+  // in-order one, whose gathers run two tiles ahead.
+  if (p.nsplit == 1) {
+    if (wide)
+      hipLaunchKernelGGL((mla_kernel<true, true>), grid, dim3(MLA_THREADS), 0, st, p);
+    else
+      hipLaunchKernelGGL((mla_kernel<false, true>), grid, dim3(MLA_THREADS), 0, st, p);
+  } else {
+    if (wide)
+      hipLaunchKernelGGL((mla_kernel<true, false>), grid, dim3(MLA_THREADS), 0, st, p);
+    else
+      hipLaunchKernelGGL((mla_kernel<false, false>), grid, dim3(MLA_THREADS), 0, st, p);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.nsplit == 1) return e;
   hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)(nq8 * 64)), dim3(256), 0, st, p.part_o, p.part_lse,
