@@ -151,7 +151,8 @@ int dsa_topk(const dsa_queries *queries, const float *scores, int64_t ld, int32_
  *   q     : bf16 [num_q, 128, 576] (absorbed query: 512 latent + 64 rotary);
  *   kv    : bf16 [R, 576] latent cache; the value is dims 0..511 of each row;
  *   idx   : int32 [num_q, k] positions; the first count[i] entries are attended
- *           (each must be < q_nvis[i]); order does not matter;
+ *           (each must be in [0, q_nvis[i])); order does not matter; an entry
+ *           outside that range is skipped (never read, not in the softmax);
  *   count : int32 [num_q], or NULL for min(k, q_nvis[i]);
  *   out   : fp32 [num_q, 128, 512] = sum_r softmax_r(z) * kv[r, 0:512] with
  *           z = softmax_scale * q . kv[r];

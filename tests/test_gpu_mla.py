@@ -116,6 +116,35 @@ def test_index_order_does_not_matter():
 
 
 @pytest.mark.parametrize("decode", [True, False])
+def test_positions_outside_history_are_skipped(decode):
+    """Entries outside [0, q_nvis) break the contract; the kernels must then
+    neither read past the cache nor let them into the softmax: the result is
+    the attention over the valid entries alone (paged cache, tiles of which
+    some are partial and some hold several such entries)."""
+    banner(f"mla out-of-range positions decode={decode}")
+    wl = make_custom(seq_lens=[3000, 900, 64], device="cuda", seed=47, paged=True)
+    idx, cnt = random_selection(wl, 2048, 6)
+    nv = wl.q_nvis.cpu().numpy()
+    rng = np.random.default_rng(7)
+    bad = idx.copy()
+    valid = []
+    for i in range(wl.nq):
+        c = int(cnt[i])
+        hit = rng.choice(c, size=min(c, 40), replace=False)
+        vals = np.where(rng.random(hit.size) < 0.5, -1 - rng.integers(0, 1000, hit.size),
+                        nv[i] + rng.integers(0, 1000, hit.size))
+        bad[i, hit] = vals
+        keep = np.ones(c, bool)
+        keep[hit] = False
+        valid.append(idx[i, :c][keep])
+    out, lse = run_mla(wl, bad, cnt, 2048, decode)
+    ov = OracleView(wl)
+    for i in range(wl.nq):
+        o_ref, l_ref = ov.mla(i, valid[i])
+        check_out(out[i], o_ref, lse[i], l_ref, f"out-of-range q{i} decode={decode}")
+
+
+@pytest.mark.parametrize("decode", [True, False])
 def test_paged_pool_beyond_4gib(decode):
     """A paged latent pool of 4.4 GB (more than 4 GiB of rows) whose block
     table alternates blocks at the start and at the end of the pool, so that
