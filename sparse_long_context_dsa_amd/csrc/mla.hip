@@ -700,13 +700,27 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const float *__restric
   if (lse && (threadIdx.x & 127) == 0) lse[(int64_t)q * 128 + head] = den > 0.0f ? mx + logf(den) : -INFINITY;
 }
 
+// Row splits per query in decode.  More splits put more of the 256 CUs to
+// work, but each writes a 256 KiB fp32 partial that the combine reads back.
+// The count minimises a time model: the busiest CU's workgroups (about 4 us
+// of prologue and epilogue, 2 us per 32-row tile), plus the partials' round
+// trip at 5 TB/s.  At least 128 rows per split.
 int mla_num_splits(int num_q, int k, bool decode) {
   if (!decode || num_q <= 0) return 1;
-  int ns = (256 + num_q - 1) / num_q;        // about one block per CU
-  const int max_split = (k + 127) / 128;     // at least 128 rows per split
-  ns = ns < 1 ? 1 : ns;
-  ns = ns > max_split ? max_split : ns;
-  return ns < 1 ? 1 : ns;
+  const int max_split = k >= 128 ? (k + 127) / 128 : 1;
+  int best_ns = 1;
+  double best = 1e300;
+  for (int ns = 1; ns <= max_split; ++ns) {
+    const double tiles = (double)((k + ns * MLA_T - 1) / (ns * MLA_T));
+    const double rounds = (double)(((int64_t)num_q * ns + 255) / 256);
+    const double partial_us = ns > 1 ? 2.0 * num_q * ns * (128.0 * 513 * 4) / 5e6 : 0.0;
+    const double t = rounds * (4.0 + 2.0 * tiles) + partial_us;
+    if (t < best) {
+      best = t;
+      best_ns = ns;
+    }
+  }
+  return best_ns;
 }
 
 static int rows_per_split(int k, int nsplit) {
