@@ -31,5 +31,5 @@ from .dsa import (  # noqa: F401
     sparse_mla,
     topk,
 )
-from .fp8 import E4M3_MAX, e4m3_decode, e4m3_encode, quantize_rows  # noqa: F401
+from .fp8 import E4M3_MAX, e4m3_decode, e4m3_encode, e8m0_decode, quantize_rows, quantize_rows_e8m0  # noqa: F401
 from .layout import phys_rows  # noqa: F401

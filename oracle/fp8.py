@@ -68,6 +68,53 @@ def e4m3_encode(x):
     return (code | np.where(neg, 0x80, 0)).astype(np.uint8)
 
 
+E8M0_BIAS = 127
+
+
+def e8m0_decode(b):
+    """E8M0 byte (an 8-bit biased exponent, no sign or mantissa) to its float64
+    value 2^(b - 127).  255 is NaN in the format and is rejected here."""
+    b = np.asarray(b, dtype=np.int64)
+    if (b == 255).any():
+        raise ValueError("E8M0 255 is NaN")
+    return np.ldexp(1.0, b - E8M0_BIAS)
+
+
+def quantize_rows_e8m0(x):
+    """Per-row FP8 quantisation with a power-of-two scale per row, the E8M0 key
+    scale of page "DeepSeekV3.2之DSA", part 4.3 (the last step multiplies the head
+    sum by k_s in e8m0).  The page does not give the rule that picks the
+    exponent; the reading taken here is the smallest power of two that keeps
+    every |x| / scale within 448, so no code saturates:
+
+        e     = min { e integer : absmax(row) <= 448 * 2^e }, clamped to [-127, 127]
+                (e = 0 for an all-zero row)
+        scale = 2^e                      (exact in fp32 and float64)
+        code  = E4M3(x / 2^e)            (an exact division, then round to nearest-even)
+        byte  = e + 127
+
+    Returns (codes uint8 [N, D], bytes uint8 [N], scales float64 [N])."""
+    x32 = np.ascontiguousarray(x, dtype=np.float32)
+    if x32.ndim != 2:
+        raise ValueError("quantize_rows_e8m0 expects a 2-D array")
+    amax = np.max(np.abs(x32.astype(np.float64)), axis=1) if x32.shape[1] else np.zeros(x32.shape[0])
+    exps = np.zeros(x32.shape[0], np.int64)
+    for i, a in enumerate(amax):
+        if a == 0.0:
+            continue
+        # Start from a float estimate, then settle it with exact comparisons
+        # (448 * 2^e is exact in float64 over the whole range).
+        e = int(np.ceil(np.log2(a / E4M3_MAX)))
+        while a > np.ldexp(E4M3_MAX, e):
+            e += 1
+        while a <= np.ldexp(E4M3_MAX, e - 1):
+            e -= 1
+        exps[i] = min(max(e, -E8M0_BIAS), E8M0_BIAS)
+    scale = np.ldexp(1.0, exps)
+    y = x32.astype(np.float64) / scale[:, None]
+    return e4m3_encode(y), (exps + E8M0_BIAS).astype(np.uint8), scale
+
+
 def quantize_rows(x):
     """Per-row FP8 quantisation of an fp32 matrix [N, D].
 

@@ -104,3 +104,62 @@ def test_quantize_rows_error_bound_and_scale():
     # the row maximum lands on (or next to) +-448
     top = np.abs(fp8.e4m3_decode(codes[ok][np.arange(ok.sum()), np.abs(x[ok]).argmax(axis=1)]))
     assert (top >= 416).all()
+
+
+# --------------------------------------------------------------- E8M0 variant
+# Pinned against the definition's closed-form properties and against PyTorch's
+# float8_e4m3fn cast of x / 2^e (an exact division, so the library cast of the
+# quotient is an independent check of the codes).
+
+
+def test_e8m0_decode_closed_form():
+    b = np.arange(255, dtype=np.uint8)
+    v = fp8.e8m0_decode(b)
+    assert (v == 2.0 ** (b.astype(np.int64) - 127)).all()
+    with pytest.raises(ValueError):
+        fp8.e8m0_decode(np.array([255], np.uint8))
+
+
+def test_e8m0_scale_is_the_smallest_power_of_two():
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((2000, 128)).astype(np.float32)
+    x *= np.float32(2.0) ** rng.integers(-40, 40, size=(2000, 1)).astype(np.float32)
+    codes, b, scale = fp8.quantize_rows_e8m0(x)
+    amax = np.abs(x.astype(np.float64)).max(axis=1)
+    assert (scale == np.ldexp(1.0, b.astype(np.int64) - 127)).all()
+    assert (amax <= 448.0 * scale).all()          # nothing saturates
+    assert (amax > 224.0 * scale).all()           # a smaller power of two would
+    # codes: the library cast of the exact quotient
+    q = (x.astype(np.float64) / scale[:, None]).astype(np.float32)
+    assert (codes == torch_encode(q)).all()
+
+
+def test_e8m0_boundaries_and_special_rows():
+    base = np.zeros((6, 64), np.float32)
+    base[0, 3] = 448.0                            # absmax = 448 * 2^0 -> e = 0, code 0x7E
+    base[1, 5] = np.float32(448.0 * 2.0 ** 10)    # exactly on a power of two -> e = 10
+    base[2, 7] = np.nextafter(np.float32(448.0 * 2.0 ** -5), np.float32(np.inf))  # just above -> e = -4
+    base[3] = 0.0                                 # all zero -> e = 0, codes 0
+    base[4, 0] = np.float32(1e-40)                # subnormal absmax -> exponent clamped at -127
+    base[5, 1] = np.float32(3e38)                 # near the fp32 maximum
+    codes, b, scale = fp8.quantize_rows_e8m0(base)
+    e = b.astype(np.int64) - 127
+    assert list(e[:4]) == [0, 10, -4, 0]
+    assert codes[0, 3] == 0x7E and codes[1, 5] == 0x7E
+    assert (codes[3] == 0).all()
+    assert e[4] == -127 and 1e-40 / scale[4] <= 448.0
+    assert 3e38 / scale[5] <= 448.0 and 3e38 / scale[5] > 224.0
+    assert (codes == torch_encode((base.astype(np.float64) / scale[:, None]).astype(np.float32))).all()
+
+
+def test_e8m0_dequantisation_error_bound():
+    """Round-to-nearest on a 3-bit mantissa: |decode(code) * 2^e - x| <= 2^-4 |x|
+    for quotients in the normal range, <= 2^-10 * 2^e below it."""
+    rng = np.random.default_rng(12)
+    x = (rng.standard_normal((500, 256)) * 3.0).astype(np.float32)
+    codes, b, scale = fp8.quantize_rows_e8m0(x)
+    back = fp8.e4m3_decode(codes) * scale[:, None]
+    err = np.abs(back - x.astype(np.float64))
+    normal = np.abs(x) / scale[:, None] >= 2.0 ** -6
+    assert (err[normal] <= 2.0 ** -4 * np.abs(x.astype(np.float64))[normal]).all()
+    assert (err[~normal] <= (2.0 ** -10 * scale[:, None] * np.ones_like(err))[~normal]).all()
