@@ -116,6 +116,19 @@ typedef enum dsa_op {
 int dsa_quantize_fp8(const float *x, int64_t rows, int32_t cols, uint8_t *codes,
                      float *scales, hipStream_t stream);
 
+/* The same quantiser with a power-of-two scale per row, the E8M0 form in which
+ * the pages' indexer kernel takes its key scales (page "DeepSeekV3.2之DSA",
+ * part 4.3, last step: the head sum times k_s in e8m0).  The page does not fix
+ * the exponent; here e is the smallest integer with absmax(row) <= 448 * 2^e
+ * (e = 0 for an all-zero row, clamped to [-127, 127]), so x / 2^e is exact and
+ * never saturates:
+ *   codes : uint8 [rows, cols] = E4M3(x / 2^e), rounded to nearest-even;
+ *   e8m0  : uint8 [rows] = e + 127;
+ *   scales: fp32 [rows] = 2^e exactly, or NULL.
+ * cols must be a multiple of 64 in [64, 512]; x and codes 16-byte aligned. */
+int dsa_quantize_fp8_e8m0(const float *x, int64_t rows, int32_t cols, uint8_t *codes,
+                          uint8_t *e8m0, float *scales, hipStream_t stream);
+
 /* Lightning-indexer scores (page "arXiv'25 | DSA ...", section 3, first
  * equation; page "DeepSeekV3.2之DSA", part 4.3, operation order):
  *   scores[i*ld + s] = k_scale[r(s)] * sum_j (w[i,j] * q_scale[i,j])
@@ -131,6 +144,16 @@ int dsa_indexer_scores(const dsa_queries *queries, const dsa_kv_layout *layout,
                        const uint8_t *q_fp8, const float *q_scale, const float *w,
                        const uint8_t *k_fp8, const float *k_scale, float *scores,
                        int64_t ld, hipStream_t stream);
+
+/* dsa_indexer_scores with the key scales as E8M0 exponents (same page, part
+ * 4.3): k_scale_e8m0 is uint8 [R], key scale 2^(b - 127) (b = 255, NaN in the
+ * format, is not a valid scale), as dsa_quantize_fp8_e8m0 writes it.  One byte
+ * per key instead of four; the scores equal dsa_indexer_scores' with the fp32
+ * scales 2^(b - 127) bit for bit. */
+int dsa_indexer_scores_e8m0(const dsa_queries *queries, const dsa_kv_layout *layout,
+                            const uint8_t *q_fp8, const float *q_scale, const float *w,
+                            const uint8_t *k_fp8, const uint8_t *k_scale_e8m0, float *scores,
+                            int64_t ld, hipStream_t stream);
 
 /* Top-k selection (page "arXiv'25 | DSA ...", section 3, second equation;
  * page "DeepSeekV3.2之DSA", part 4.4: indices of the min(topk, end_pos) largest

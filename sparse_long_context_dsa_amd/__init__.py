@@ -20,7 +20,8 @@ from ._lib import (  # noqa: F401
 )
 
 __all__ = [
-    "HipEvents", "Queries", "KvLayout", "dsa_quantize_fp8", "dsa_indexer_scores", "dsa_topk",
+    "HipEvents", "Queries", "KvLayout", "dsa_quantize_fp8", "dsa_quantize_fp8_e8m0", "dsa_indexer_scores",
+    "dsa_indexer_scores_e8m0", "dsa_topk",
     "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill", "dsa_forward", "dsa_workspace_bytes",
     "workspace", "lib_path",
 ]
@@ -112,6 +113,33 @@ def dsa_quantize_fp8(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor,
     _need(scales, torch.float32, (rows,), "scales")
     _lib.check("dsa_quantize_fp8", _lib.lib().dsa_quantize_fp8(
         _ptr(x), rows, cols, _ptr(codes), _ptr(scales), _stream(stream)))
+
+
+def dsa_quantize_fp8_e8m0(x: torch.Tensor, codes: torch.Tensor, e8m0: torch.Tensor, scales=None, stream=None):
+    rows, cols = x.shape
+    _need(x, torch.float32, None, "x")
+    _need(codes, torch.uint8, (rows, cols), "codes")
+    _need(e8m0, torch.uint8, (rows,), "e8m0")
+    if scales is not None:
+        _need(scales, torch.float32, (rows,), "scales")
+    _lib.check("dsa_quantize_fp8_e8m0", _lib.lib().dsa_quantize_fp8_e8m0(
+        _ptr(x), rows, cols, _ptr(codes), _ptr(e8m0), _ptr(scales), _stream(stream)))
+
+
+def dsa_indexer_scores_e8m0(queries: Queries, layout: KvLayout, q_fp8, q_scale, w, k_fp8, k_scale_e8m0,
+                            scores, stream=None):
+    nq = queries.num_q
+    _need(q_fp8, torch.uint8, (nq, DSA_HI, DSA_DI), "q_fp8")
+    if q_scale is not None:
+        _need(q_scale, torch.float32, (nq, DSA_HI), "q_scale")
+    _need(w, torch.float32, (nq, DSA_HI), "w")
+    _need(k_fp8, torch.uint8, (layout.num_rows, DSA_DI), "k_fp8")
+    _need(k_scale_e8m0, torch.uint8, (layout.num_rows,), "k_scale_e8m0")
+    _need(scores, torch.float32, None, "scores")
+    qc, lc = queries.c(), layout.c()
+    _lib.check("dsa_indexer_scores_e8m0", _lib.lib().dsa_indexer_scores_e8m0(
+        ctypes.byref(qc), ctypes.byref(lc), _ptr(q_fp8), _ptr(q_scale), _ptr(w), _ptr(k_fp8),
+        _ptr(k_scale_e8m0), _ptr(scores), scores.shape[1], _stream(stream)))
 
 
 def dsa_indexer_scores(queries: Queries, layout: KvLayout, q_fp8, q_scale, w, k_fp8, k_scale,

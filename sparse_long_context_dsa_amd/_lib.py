@@ -15,7 +15,9 @@ DSA_OP_TOPK, DSA_OP_MLA_DECODE, DSA_OP_MLA_PREFILL, DSA_OP_FORWARD = 1, 2, 3, 4
 
 EXPORTED = (
     "dsa_quantize_fp8",
+    "dsa_quantize_fp8_e8m0",
     "dsa_indexer_scores",
+    "dsa_indexer_scores_e8m0",
     "dsa_topk",
     "dsa_sparse_mla_decode",
     "dsa_sparse_mla_prefill",
@@ -71,7 +73,9 @@ def lib():
     qp, lp = ctypes.POINTER(QueriesC), ctypes.POINTER(KvLayoutC)
     sig = {
         "dsa_quantize_fp8": [vp, i64, i32, vp, vp, vp],
+        "dsa_quantize_fp8_e8m0": [vp, i64, i32, vp, vp, vp, vp],
         "dsa_indexer_scores": [qp, lp, vp, vp, vp, vp, vp, vp, i64, vp],
+        "dsa_indexer_scores_e8m0": [qp, lp, vp, vp, vp, vp, vp, vp, i64, vp],
         "dsa_topk": [qp, vp, i64, i32, vp, vp, vp, sz, vp],
         "dsa_sparse_mla_decode": [qp, lp, vp, vp, vp, vp, i32, f32, vp, vp, vp, sz, vp],
         "dsa_sparse_mla_prefill": [qp, lp, vp, vp, vp, vp, i32, f32, vp, vp, vp, sz, vp],

@@ -153,22 +153,45 @@ int dsa_quantize_fp8(const float *x, int64_t rows, int32_t cols, uint8_t *codes,
   return hip_status(dsa::launch_quantize_fp8(x, rows, cols, codes, scales, stream), "quantize launch");
 }
 
-int dsa_indexer_scores(const dsa_queries *qr, const dsa_kv_layout *ly, const uint8_t *q_fp8, const float *q_scale,
-                       const float *w, const uint8_t *k_fp8, const float *k_scale, float *scores, int64_t ld,
-                       hipStream_t stream) {
+int dsa_quantize_fp8_e8m0(const float *x, int64_t rows, int32_t cols, uint8_t *codes, uint8_t *e8m0,
+                          float *scales, hipStream_t stream) {
+  if (rows < 0) return fail(DSA_ERR_INVALID_ARG, "rows = %lld < 0", (long long)rows);
+  if (cols < 64 || cols > 512 || cols % 64 != 0)
+    return fail(DSA_ERR_UNSUPPORTED, "cols = %d: must be a multiple of 64 in [64, 512]", cols);
+  if (rows == 0) return ok();
+  if (!x || !codes || !e8m0) return fail(DSA_ERR_INVALID_ARG, "x, codes and e8m0 must be non-NULL");
+  if (!aligned(x, 16) || !aligned(codes, 16)) return fail(DSA_ERR_INVALID_ARG, "x and codes must be 16-byte aligned");
+  return hip_status(dsa::launch_quantize_fp8_e8m0(x, rows, cols, codes, e8m0, scales, stream), "quantize launch");
+}
+
+static int indexer_impl(const dsa_queries *qr, const dsa_kv_layout *ly, const uint8_t *q_fp8, const float *q_scale,
+                        const float *w, const uint8_t *k_fp8, const float *k_scale, const uint8_t *k_e8m0,
+                        float *scores, int64_t ld, hipStream_t stream) {
   int st;
   if ((st = check_queries(qr))) return st;
   dsa::KvMap m;
   if ((st = check_layout(ly, m))) return st;
   if (qr->num_q == 0 || qr->max_nvis == 0) return ok();
-  if (!q_fp8 || !w || !k_fp8 || !k_scale || !scores)
-    return fail(DSA_ERR_INVALID_ARG, "q_fp8, w, k_fp8, k_scale and scores must be non-NULL");
+  if (!q_fp8 || !w || !k_fp8 || !(k_scale || k_e8m0) || !scores)
+    return fail(DSA_ERR_INVALID_ARG, "q_fp8, w, k_fp8, the key scales and scores must be non-NULL");
   if (ld < qr->max_nvis || ld % 4 != 0) return fail(DSA_ERR_INVALID_ARG, "ld = %lld: need ld >= max_nvis and ld %% 4 == 0", (long long)ld);
   if (!aligned(q_fp8, 16) || !aligned(k_fp8, 16) || !aligned(scores, 16))
     return fail(DSA_ERR_INVALID_ARG, "q_fp8, k_fp8 and scores must be 16-byte aligned");
   dsa::IndexerLaunch a{q_fp8, q_scale, w, k_fp8, k_scale, qr->q_seq, qr->q_nvis, m, scores, ld, nullptr, -1,
-                       qr->num_q, qr->max_nvis};
+                       qr->num_q, qr->max_nvis, k_e8m0};
   return hip_status(dsa::launch_indexer(a, stream), "indexer launch");
+}
+
+int dsa_indexer_scores(const dsa_queries *qr, const dsa_kv_layout *ly, const uint8_t *q_fp8, const float *q_scale,
+                       const float *w, const uint8_t *k_fp8, const float *k_scale, float *scores, int64_t ld,
+                       hipStream_t stream) {
+  return indexer_impl(qr, ly, q_fp8, q_scale, w, k_fp8, k_scale, nullptr, scores, ld, stream);
+}
+
+int dsa_indexer_scores_e8m0(const dsa_queries *qr, const dsa_kv_layout *ly, const uint8_t *q_fp8,
+                            const float *q_scale, const float *w, const uint8_t *k_fp8, const uint8_t *k_scale_e8m0,
+                            float *scores, int64_t ld, hipStream_t stream) {
+  return indexer_impl(qr, ly, q_fp8, q_scale, w, k_fp8, nullptr, k_scale_e8m0, scores, ld, stream);
 }
 
 int dsa_topk(const dsa_queries *qr, const float *scores, int64_t ld, int32_t k, int32_t *idx, int32_t *count,

@@ -25,6 +25,9 @@ __device__ __forceinline__ int64_t phys_row(const KvMap &m, int seq, int s) {
 // ---------------------------------------------------------------- launchers
 hipError_t launch_quantize_fp8(const float *x, int64_t rows, int cols, uint8_t *codes,
                                float *scales, hipStream_t st);
+// Power-of-two scales: e8m0[row] = e + 127, scales[row] = 2^e (scales may be null).
+hipError_t launch_quantize_fp8_e8m0(const float *x, int64_t rows, int cols, uint8_t *codes,
+                                    uint8_t *e8m0, float *scales, hipStream_t st);
 
 struct IndexerLaunch {
   const uint8_t *q8;
@@ -41,6 +44,7 @@ struct IndexerLaunch {
   int32_t skip_le;       // queries with n_vis <= skip_le are not scored (-1: none)
   int32_t num_q;
   int32_t max_nvis;
+  const uint8_t *k_e8m0;  // key scales as E8M0 exponents instead of k_scale (null: use k_scale)
 };
 hipError_t launch_indexer(const IndexerLaunch &a, hipStream_t st);
 

@@ -7,7 +7,9 @@
 // weight, sum over heads, times the key scale).  q_scale is folded into the
 // head weight (same page, part 4.3: the weights carry the q scale); the key
 // scale is applied after the head sum, which is exact reordering because
-// k_scale > 0 and ReLU is positively homogeneous.
+// k_scale > 0 and ReLU is positively homogeneous.  The key scales come either
+// as fp32 or, as in that page's kernel, as E8M0 exponents (one byte per key,
+// scale 2^(b - 127)): 133 instead of 136 bytes per key.
 //
 // Mapping: one wavefront owns one query and a run of kpw keys.  The 64
 // indexer heads are the M side of v_mfma_scale_f32_16x16x128_f8f6f4 (4 M-tiles
@@ -57,18 +59,24 @@ struct KeyStep {
   float ks;
 };
 
+// E8M0 byte b -> 2^(b - 127) (b = 0 is the subnormal 2^-127; 255 is not a scale).
+__device__ __forceinline__ float e8m0_value(uint32_t b) {
+  return __uint_as_float(b ? b << 23 : 0x00400000u);
+}
+
 // Loads the B operands (4 tiles of 16 keys) of the 64-key step at s0, whose
 // keys sit in the physical rows base .. base + 63.  Keys at or past nvis read
 // the step's last visible row instead: every lane always issues the same
 // loads (no branch, so the compiler's wait counts stay exact), and the scores
 // of those keys are never stored.
+template <bool E8M0>
 __device__ __forceinline__ void load_step(const IndexerLaunch &a, int64_t base, int s0, int nvis, int lane,
                                           KeyStep &st) {
   const int sub = lane & 15, half = lane >> 4;
   const int last = nvis - 1 - s0;  // >= 0
 #pragma unroll
   for (int t = 0; t < 4; ++t) st.b[t] = load32(a.k8 + (base + min(16 * t + sub, last)) * 128 + 32 * half);
-  st.ks = a.k_scale[base + min(lane, last)];
+  st.ks = E8M0 ? e8m0_value(a.k_e8m0[base + min(lane, last)]) : a.k_scale[base + min(lane, last)];
 }
 
 __device__ __forceinline__ float relu(float x) {
@@ -77,7 +85,7 @@ __device__ __forceinline__ float relu(float x) {
   return r;
 }
 
-template <bool HIST>
+template <bool HIST, bool E8M0>
 __global__ __launch_bounds__(256) void indexer_kernel(IndexerLaunch a, int nchunks, int kpw) {
   const int q = blockIdx.x / nchunks;
   const int chunk = blockIdx.x - q * nchunks;
@@ -153,7 +161,7 @@ __global__ __launch_bounds__(256) void indexer_kernel(IndexerLaunch a, int nchun
   // group, score the keys in `cur`.  The loop alternates two buffers, so no
   // register copy forces an early wait on the prefetch.
   auto step = [&](int s0, const KeyStep &cur, KeyStep *nxt) {
-    if (nxt) load_step(a, readlane64(lane_row, ((s0 - s_begin) >> 6) + 1), s0 + 64, nvis, lane, *nxt);
+    if (nxt) load_step<E8M0>(a, readlane64(lane_row, ((s0 - s_begin) >> 6) + 1), s0 + 64, nvis, lane, *nxt);
     if (pending >= 0) {
       flush(pending);
       pending = -1;
@@ -187,7 +195,7 @@ __global__ __launch_bounds__(256) void indexer_kernel(IndexerLaunch a, int nchun
   // last one or two are peeled, so the prefetch in the loop is unconditional.
   const int nsteps = s_begin < s_end ? (s_end - s_begin + 63) >> 6 : 0;
   KeyStep kb0, kb1;
-  if (nsteps > 0) load_step(a, readlane64(lane_row, 0), s_begin, nvis, lane, kb0);
+  if (nsteps > 0) load_step<E8M0>(a, readlane64(lane_row, 0), s_begin, nvis, lane, kb0);
   int i = 0;
   for (; i + 2 < nsteps; i += 2) {
     step(s_begin + 64 * i, kb0, &kb1);
@@ -225,12 +233,18 @@ hipError_t launch_indexer(const IndexerLaunch &a, hipStream_t st) {
   }
   const int nchunks = (a.max_nvis + IDX_WAVES * kpw - 1) / (IDX_WAVES * kpw);
   const int64_t blocks = (int64_t)a.num_q * nchunks;
-  if (a.hist)
-    hipLaunchKernelGGL(indexer_kernel<true>, dim3((unsigned)blocks), dim3(IDX_WAVES * WAVE), 0, st, a,
-                       nchunks, kpw);
-  else
-    hipLaunchKernelGGL(indexer_kernel<false>, dim3((unsigned)blocks), dim3(IDX_WAVES * WAVE), 0, st, a,
-                       nchunks, kpw);
+  const dim3 grid((unsigned)blocks), block(IDX_WAVES * WAVE);
+  if (a.k_e8m0) {
+    if (a.hist)
+      hipLaunchKernelGGL((indexer_kernel<true, true>), grid, block, 0, st, a, nchunks, kpw);
+    else
+      hipLaunchKernelGGL((indexer_kernel<false, true>), grid, block, 0, st, a, nchunks, kpw);
+  } else {
+    if (a.hist)
+      hipLaunchKernelGGL((indexer_kernel<true, false>), grid, block, 0, st, a, nchunks, kpw);
+    else
+      hipLaunchKernelGGL((indexer_kernel<false, false>), grid, block, 0, st, a, nchunks, kpw);
+  }
   return hipGetLastError();
 }
 

@@ -66,13 +66,17 @@ class OracleView:
         return oracle.phys_rows(int(self.q_seq[i]), pos, row0=self.row0, block_table=self.bt,
                                 block_size=self.wl.block_size)
 
-    def indexer(self, i):
-        """(I, M) of query i over its whole visible history, float64."""
+    def indexer(self, i, e8m0=False):
+        """(I, M) of query i over its whole visible history, float64; with
+        e8m0, the keys carry the power-of-two scales of the E8M0 quantiser."""
         wl = self.wl
         q8, qs = oracle.quantize_rows(wl.q_idx[i].cpu().numpy())
         r = self.rows(i)
         keys = wl.k_idx[torch.from_numpy(r).to(wl.k_idx.device)].cpu().numpy() if r.size else np.zeros((0, 128), np.float32)
-        k8, ks = oracle.quantize_rows(keys)
+        if e8m0:
+            k8, _, ks = oracle.quantize_rows_e8m0(keys)
+        else:
+            k8, ks = oracle.quantize_rows(keys)
         return oracle.indexer_scores_query(q8, qs, wl.w[i].cpu().numpy(), k8, ks)
 
     def mla(self, i, positions):

@@ -84,3 +84,54 @@ def test_exact_grid_values_bit_exact():
     for i in range(nq):
         ref, _ = oracle.indexer_scores_query(q8[i], qs[i], w[i], k8[i * L:(i + 1) * L], ks[i * L:(i + 1) * L])
         assert (host[i, :L].astype(np.float64) == ref).all()
+
+
+def e8m0_inputs(wl):
+    """Device inputs with the keys quantised by the E8M0 variant: codes, bytes
+    and the equal fp32 scales 2^(b - 127)."""
+    g = GpuInputs(wl)
+    k8 = torch.empty_like(g.k8)
+    kb = torch.empty((wl.rows,), dtype=torch.uint8, device=k8.device)
+    ks = torch.empty((wl.rows,), dtype=torch.float32, device=k8.device)
+    dsa.dsa_quantize_fp8_e8m0(wl.k_idx, k8, kb, ks)
+    return g, k8, kb, ks
+
+
+def test_e8m0_key_scales_against_oracle():
+    """dsa_indexer_scores_e8m0 on keys quantised with power-of-two scales,
+    against the oracle fed the same E8M0 quantisation (ragged paged decode)."""
+    banner("indexer e8m0 key scales")
+    wl = make_custom(seq_lens=[1, 63, 65, 3000, 9000], device="cuda", seed=15, paged=True, plant=True)
+    g, k8, kb, _ = e8m0_inputs(wl)
+    ld = (wl.max_nvis + 63) // 64 * 64
+    s = torch.full((wl.nq, ld), float("nan"), dtype=torch.float32, device="cuda")
+    dsa.dsa_indexer_scores_e8m0(g.queries, g.layout, g.q8, g.qs, wl.w, k8, kb, s)
+    torch.cuda.synchronize()
+    host = s.cpu().numpy()
+    nv = wl.q_nvis.cpu().numpy()
+    ov = OracleView(wl)
+    for i in range(wl.nq):
+        ref, mag = ov.indexer(i, e8m0=True)
+        n = int(nv[i])
+        check_scores(host[i, :n], ref, mag, f"e8m0 query {i}")
+        assert np.isnan(host[i, n:]).all()
+
+
+def test_e8m0_equals_fp32_power_of_two_scales_bit_exact():
+    """The E8M0 entry point and the fp32 one given the same scales 2^(b - 127)
+    compute the same thing: the scores must agree bit for bit (decode 4 x 20000
+    and a prefill batch)."""
+    banner("indexer e8m0 vs fp32 scales")
+    for wl in (make_custom(seq_lens=[20000] * 4, device="cuda", seed=16),
+               make_custom(seq_lens=[3000], device="cuda", seed=17, prefill=True, queries_per_seq=64)):
+        g, k8, kb, ks = e8m0_inputs(wl)
+        ld = (wl.max_nvis + 63) // 64 * 64
+        a = torch.full((wl.nq, ld), float("nan"), dtype=torch.float32, device="cuda")
+        b = torch.full((wl.nq, ld), float("nan"), dtype=torch.float32, device="cuda")
+        dsa.dsa_indexer_scores_e8m0(g.queries, g.layout, g.q8, g.qs, wl.w, k8, kb, a)
+        dsa.dsa_indexer_scores(g.queries, g.layout, g.q8, g.qs, wl.w, k8, ks, b)
+        torch.cuda.synchronize()
+        av, bv = a.cpu().numpy(), b.cpu().numpy()
+        assert (np.isnan(av) == np.isnan(bv)).all()
+        fin = ~np.isnan(av)
+        assert (av[fin].view(np.uint32) == bv[fin].view(np.uint32)).all()

@@ -58,3 +58,45 @@ def test_special_rows_bit_exact():
     rc, rs = oracle.quantize_rows(x)
     assert (scales.view(np.uint32) == rs.view(np.uint32)).all()
     assert (codes == rc).all(), np.argwhere(codes != rc)[:10]
+
+
+def run_e8m0(x, with_scales=True):
+    xd = torch.from_numpy(x).cuda()
+    codes = torch.empty(x.shape, dtype=torch.uint8, device="cuda")
+    e8m0 = torch.empty(x.shape[0], dtype=torch.uint8, device="cuda")
+    scales = torch.empty(x.shape[0], dtype=torch.float32, device="cuda") if with_scales else None
+    dsa.dsa_quantize_fp8_e8m0(xd, codes, e8m0, scales)
+    torch.cuda.synchronize()
+    return codes.cpu().numpy(), e8m0.cpu().numpy(), (scales.cpu().numpy() if with_scales else None)
+
+
+@pytest.mark.parametrize("cols", [64, 128, 512])
+def test_e8m0_random_rows_bit_exact(cols):
+    banner(f"quantize e8m0 random rows cols={cols}")
+    rng = np.random.default_rng(100 + cols)
+    x = rng.standard_normal((3001, cols)).astype(np.float32)
+    x *= (np.float32(2.0) ** rng.integers(-60, 60, size=(3001, 1))).astype(np.float32)
+    codes, b, scales = run_e8m0(x)
+    rc, rb, rs = oracle.quantize_rows_e8m0(x)
+    assert (b == rb).all(), np.argwhere(b != rb)[:10]
+    assert (scales.astype(np.float64) == rs).all()
+    assert (codes == rc).all(), f"{(codes != rc).sum()} codes differ"
+
+
+def test_e8m0_special_rows_bit_exact():
+    banner("quantize e8m0 special rows")
+    x = np.zeros((8, 64), np.float32)
+    x[0, 3] = 448.0                                   # e = 0, code 0x7E
+    x[1, 5] = np.float32(448.0 * 2.0 ** 10)           # exactly 448 * 2^10
+    x[2, 7] = np.nextafter(np.float32(448.0 * 2.0 ** -5), np.float32(np.inf))  # just above a boundary
+    x[3] = -0.0                                       # all -0: e = 0, codes 0x80
+    x[4, 0] = np.float32(1e-40)                       # subnormal absmax: exponent clamped at -127
+    x[5, 1] = np.float32(-3e38)                       # near the fp32 maximum
+    x[6] = np.linspace(-7, 7, 64).astype(np.float32)  # m > 1.75 case (absmax 7 = 1.75 * 4)
+    x[7] = np.linspace(-7.5, 7.5, 64).astype(np.float32)
+    codes, b, scales = run_e8m0(x)
+    rc, rb, rs = oracle.quantize_rows_e8m0(x)
+    assert (b == rb).all() and (scales.astype(np.float64) == rs).all()
+    assert (codes == rc).all(), np.argwhere(codes != rc)[:10]
+    codes2, b2, _ = run_e8m0(x, with_scales=False)    # scales are optional
+    assert (codes2 == codes).all() and (b2 == b).all()
