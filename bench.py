@@ -148,6 +148,42 @@ def time_forward(wl, p, steps, warmup):
     return wall, {k: float(np.mean(v)) for k, v in st.items()}, wall_ev
 
 
+def key_scale_formats(wl, p, steps):
+    """The standalone indexer (no histogram) on the same workload with fp32 key
+    scales and with E8M0 key scales (one byte per key, from
+    dsa_quantize_fp8_e8m0): mean launch time over `steps` launches, each between
+    torch CUDA events on the stream the library launches on."""
+    import sparse_long_context_dsa_amd as dsa
+    nq, rows = wl.nq, wl.rows
+    k8e = torch.empty((rows, 128), dtype=torch.uint8, device="cuda")
+    kb = torch.empty((rows,), dtype=torch.uint8, device="cuda")
+    dsa.dsa_quantize_fp8_e8m0(wl.k_idx, k8e, kb)
+    ld = (wl.max_nvis + 63) // 64 * 64
+    scores = torch.empty((nq, ld), dtype=torch.float32, device="cuda")
+    units = indexer_units(wl.q_nvis.cpu().numpy(), -1)
+    res = {}
+    for name, call, per_key in (
+            ("fp32_key_scales", lambda: dsa.dsa_indexer_scores(p["queries"], p["layout"], p["q8"], p["qs"], wl.w,
+                                                               p["k8"], p["ks"], scores), 128 + 4 + 4),
+            ("e8m0_key_scales", lambda: dsa.dsa_indexer_scores_e8m0(p["queries"], p["layout"], p["q8"], p["qs"],
+                                                                    wl.w, k8e, kb, scores), 128 + 1 + 4)):
+        for _ in range(3):
+            call()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        torch.cuda.synchronize()
+        for e0, e1 in evs:
+            e0.record()
+            call()
+            e1.record()
+        torch.cuda.synchronize()
+        ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+        nbytes = units * per_key + nq * (64 * 128 + 64 * 8)
+        res[name] = {"us": 1e3 * ms, "bytes_per_launch": nbytes, "gbs": nbytes / (ms * 1e-3) / 1e9,
+                     "frac_hbm": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    del k8e, kb, scores
+    return res
+
+
 def cpu_baseline(wl, sample, k):
     """The oracle (NumPy float64) on the first `sample` queries of the workload.
     Its inputs (FP8 codes from its own quantiser, bf16 rows) are prepared
@@ -285,6 +321,8 @@ def decode_result(args):
     })
     if traffic is not None:
         result["roofline"]["traffic_bytes_per_launch"] = INDEXER_TRAFFIC["bytes_per_launch"]
+    log("standalone indexer: fp32 vs E8M0 key scales")
+    result["indexer_key_scales"] = key_scale_formats(wl, p, args.steps)
     if args.copy_calib:
         log("calibration copy")
         calibration_copy()
