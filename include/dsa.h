@@ -101,7 +101,8 @@ typedef enum dsa_op {
   DSA_OP_TOPK = 1,
   DSA_OP_MLA_DECODE = 2,
   DSA_OP_MLA_PREFILL = 3,
-  DSA_OP_FORWARD = 4
+  DSA_OP_FORWARD = 4,
+  DSA_OP_MLA_DENSE = 5     /* k is not used (any value in [1, 2048]) */
 } dsa_op;
 
 /* Per-row FP8 E4M3 quantisation, the step that writes the indexer's q and
@@ -191,6 +192,18 @@ int dsa_sparse_mla_decode(const dsa_queries *queries, const dsa_kv_layout *layou
                           const int32_t *count, int32_t k, float softmax_scale,
                           float *out, float *lse, void *ws, size_t ws_bytes,
                           hipStream_t stream);
+/* Dense mode: the same attention over every visible position [0, q_nvis[i])
+ * of each query, with no indexer and no selection.  It is the pages'
+ * short-context variant (page "arXiv'25 | DSA ...", section 6: short prefill
+ * runs a dense masked attention that emulates DSA; page "DeepSeekV3.2之DSA",
+ * part 4.5: a history no longer than k keeps every position), and the other
+ * side of the sparse-versus-dense crossover.  Histories up to 2^20 positions;
+ * longer ones are split over workgroups and merged, as in _decode.
+ *   q, kv, out, lse : as for dsa_sparse_mla_decode;
+ *   ws : dsa_workspace_bytes(DSA_OP_MLA_DENSE, queries, 1) bytes. */
+int dsa_dense_mla(const dsa_queries *queries, const dsa_kv_layout *layout, const uint16_t *q,
+                  const uint16_t *kv, float softmax_scale, float *out, float *lse, void *ws,
+                  size_t ws_bytes, hipStream_t stream);
 int dsa_sparse_mla_prefill(const dsa_queries *queries, const dsa_kv_layout *layout,
                            const uint16_t *q, const uint16_t *kv, const int32_t *idx,
                            const int32_t *count, int32_t k, float softmax_scale,

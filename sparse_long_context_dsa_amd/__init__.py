@@ -16,13 +16,13 @@ import torch
 from . import _lib
 from ._lib import (  # noqa: F401
     DSA_D, DSA_DI, DSA_DV, DSA_H, DSA_HI, DSA_KMAX, DSA_OP_FORWARD, DSA_OP_MLA_DECODE,
-    DSA_OP_MLA_PREFILL, DSA_OP_TOPK, DsaError, KvLayoutC, QueriesC,
+    DSA_OP_MLA_DENSE, DSA_OP_MLA_PREFILL, DSA_OP_TOPK, DsaError, KvLayoutC, QueriesC,
 )
 
 __all__ = [
     "HipEvents", "Queries", "KvLayout", "dsa_quantize_fp8", "dsa_quantize_fp8_e8m0", "dsa_indexer_scores",
     "dsa_indexer_scores_e8m0", "dsa_topk",
-    "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill", "dsa_forward", "dsa_workspace_bytes",
+    "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill", "dsa_dense_mla", "dsa_forward", "dsa_workspace_bytes",
     "workspace", "lib_path",
 ]
 
@@ -203,6 +203,23 @@ def dsa_sparse_mla_prefill(queries, layout, q, kv, idx, count, k, softmax_scale,
                            stream=None):
     return _mla("dsa_sparse_mla_prefill", DSA_OP_MLA_PREFILL, queries, layout, q, kv, idx, count, k,
                 softmax_scale, out, lse, ws, stream)
+
+
+def dsa_dense_mla(queries, layout, q, kv, softmax_scale, out, lse=None, ws=None, stream=None):
+    """Attention over every visible position of each query (no selection)."""
+    nq = queries.num_q
+    _need(q, torch.bfloat16, (nq, DSA_H, DSA_D), "q")
+    _need(kv, torch.bfloat16, (layout.num_rows, DSA_D), "kv")
+    _need(out, torch.float32, (nq, DSA_H, DSA_DV), "out")
+    if lse is not None:
+        _need(lse, torch.float32, (nq, DSA_H), "lse")
+    if ws is None:
+        ws = workspace(DSA_OP_MLA_DENSE, queries, 1, q.device)
+    qc, lc = queries.c(), layout.c()
+    _lib.check("dsa_dense_mla", _lib.lib().dsa_dense_mla(
+        ctypes.byref(qc), ctypes.byref(lc), _ptr(q), _ptr(kv), float(softmax_scale), _ptr(out), _ptr(lse),
+        _ptr(ws), ws.numel(), _stream(stream)))
+    return ws
 
 
 def dsa_forward(queries: Queries, layout: KvLayout, q_fp8, q_scale, w, k_fp8, k_scale, q, kv, k,

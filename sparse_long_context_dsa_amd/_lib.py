@@ -11,7 +11,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdsa.so")
 
 DSA_HI, DSA_DI, DSA_H, DSA_D, DSA_DV, DSA_KMAX = 64, 128, 128, 576, 512, 2048
 DSA_OK, DSA_ERR_INVALID_ARG, DSA_ERR_UNSUPPORTED, DSA_ERR_WORKSPACE, DSA_ERR_HIP = 0, 1, 2, 3, 4
-DSA_OP_TOPK, DSA_OP_MLA_DECODE, DSA_OP_MLA_PREFILL, DSA_OP_FORWARD = 1, 2, 3, 4
+DSA_OP_TOPK, DSA_OP_MLA_DECODE, DSA_OP_MLA_PREFILL, DSA_OP_FORWARD, DSA_OP_MLA_DENSE = 1, 2, 3, 4, 5
 
 EXPORTED = (
     "dsa_quantize_fp8",
@@ -21,6 +21,7 @@ EXPORTED = (
     "dsa_topk",
     "dsa_sparse_mla_decode",
     "dsa_sparse_mla_prefill",
+    "dsa_dense_mla",
     "dsa_forward",
     "dsa_forward_profiled",
     "dsa_workspace_bytes",
@@ -79,6 +80,7 @@ def lib():
         "dsa_topk": [qp, vp, i64, i32, vp, vp, vp, sz, vp],
         "dsa_sparse_mla_decode": [qp, lp, vp, vp, vp, vp, i32, f32, vp, vp, vp, sz, vp],
         "dsa_sparse_mla_prefill": [qp, lp, vp, vp, vp, vp, i32, f32, vp, vp, vp, sz, vp],
+        "dsa_dense_mla": [qp, lp, vp, vp, f32, vp, vp, vp, sz, vp],
         "dsa_forward": [qp, lp, vp, vp, vp, vp, vp, vp, vp, i32, f32, vp, vp, vp, vp, sz, vp],
         "dsa_forward_profiled": [qp, lp, vp, vp, vp, vp, vp, vp, vp, i32, f32, vp, vp, vp, vp, sz, vp, vp],
         "dsa_workspace_bytes": [ctypes.c_int, qp, i32],

@@ -229,6 +229,25 @@ int dsa_sparse_mla_prefill(const dsa_queries *qr, const dsa_kv_layout *ly, const
   return mla_common(false, qr, ly, q, kv, idx, count, k, softmax_scale, out, lse, ws, ws_bytes, stream);
 }
 
+int dsa_dense_mla(const dsa_queries *qr, const dsa_kv_layout *ly, const uint16_t *q, const uint16_t *kv,
+                  float softmax_scale, float *out, float *lse, void *ws, size_t ws_bytes, hipStream_t stream) {
+  int st;
+  if ((st = check_queries(qr))) return st;
+  dsa::KvMap m;
+  if ((st = check_layout(ly, m))) return st;
+  if (qr->num_q == 0) return ok();
+  if (!q || !kv || !out) return fail(DSA_ERR_INVALID_ARG, "q, kv and out must be non-NULL");
+  if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(out, 16))
+    return fail(DSA_ERR_INVALID_ARG, "q, kv and out must be 16-byte aligned");
+  const int longest = qr->max_nvis > 0 ? qr->max_nvis : 1;
+  const size_t need = dsa::mla_ws_bytes(qr->num_q, longest, true, true);
+  if (need > 0 && (!ws || ws_bytes < need || !aligned(ws, 256)))
+    return fail(DSA_ERR_WORKSPACE, "workspace: need %zu bytes (256-byte aligned), got %zu", need, ws_bytes);
+  dsa::MlaLaunch a{q, kv, nullptr, nullptr, qr->q_seq, qr->q_nvis, m, longest, qr->num_q, softmax_scale, out, lse,
+                   ly->num_rows, true};
+  return hip_status(dsa::launch_mla(a, true, ws, stream), "dense MLA launch");
+}
+
 static int forward_impl(const dsa_queries *qr, const dsa_kv_layout *ly, const uint8_t *q_fp8, const float *q_scale,
                         const float *w, const uint8_t *k_fp8, const float *k_scale, const uint16_t *q,
                         const uint16_t *kv, int32_t k, float softmax_scale, float *out, float *lse, int32_t *idx_out,
@@ -295,7 +314,9 @@ int dsa_forward_profiled(const dsa_queries *qr, const dsa_kv_layout *ly, const u
 }
 
 size_t dsa_workspace_bytes(int op, const dsa_queries *qr, int32_t k) {
-  if (!qr || qr->num_q < 0 || qr->max_nvis < 0 || k < 1 || k > DSA_KMAX) return SIZE_MAX;
+  if (!qr || qr->num_q < 0 || qr->max_nvis < 0) return SIZE_MAX;
+  if (op == DSA_OP_MLA_DENSE) return dsa::mla_ws_bytes(qr->num_q, qr->max_nvis > 0 ? qr->max_nvis : 1, true, true);
+  if (k < 1 || k > DSA_KMAX) return SIZE_MAX;
   switch (op) {
     case DSA_OP_TOPK:
       return dsa::topk_ws_bytes(qr->num_q, qr->max_nvis);

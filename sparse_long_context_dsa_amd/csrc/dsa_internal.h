@@ -91,9 +91,14 @@ struct MlaLaunch {
   float *out;
   float *lse;            // may be null
   int64_t num_rows;      // rows of the latent cache
+  bool dense;            // every visible position, no idx (k = the longest history)
 };
 int mla_num_splits(int num_q, int k, bool decode);
-size_t mla_ws_bytes(int num_q, int k, bool decode);
+// Row splits of the dense mode: the time model, with at most 2080 tiles of 32
+// rows per workgroup (its per-tile row table lives in LDS).
+int mla_dense_splits(int num_q, int max_nvis);
+// dense: the workspace of the dense mode, k being the longest history.
+size_t mla_ws_bytes(int num_q, int k, bool decode, bool dense = false);
 hipError_t launch_mla(const MlaLaunch &a, bool decode, void *ws, hipStream_t st);
 
 }  // namespace dsa

@@ -64,6 +64,7 @@ struct MlaKernelArgs {
   float scale_log2;
   float *part_o;    // [num_q, nsplit, 128, 512]   (nsplit > 1)
   float *part_lse;  // [num_q, nsplit, 128]
+  int dense;        // prow holds the base row of each 32-row tile of positions
 };
 
 __device__ __forceinline__ v8bf as_bf(const uint4 &u) { return __builtin_bit_cast(v8bf, u); }
@@ -164,10 +165,13 @@ __device__ __forceinline__ void read_head_values(const float *x, int g, float *v
 // tile_row gives the lane's source row; issue_part issues part i of the
 // gather (so that a caller can spread the parts between other work).
 // Rows of a partial last tile past `last` repeat row `last` (finite data,
-// masked out of the softmax).
-__device__ __forceinline__ uint32_t tile_row(const uint32_t *prow, int r0, bool real, int last, int wave,
-                                             int lane) {
-  return prow[real ? min(r0 + 8 * wave + (lane >> 3), last) : 0] & ~INVALID_ROW;
+// masked out of the softmax).  In the dense mode prow holds one base row per
+// 32-row tile instead (positions are consecutive, and a tile never straddles
+// a cache block).
+__device__ __forceinline__ uint32_t tile_row(const uint32_t *prow, int r0, bool real, int last, bool dense,
+                                             int wave, int lane) {
+  const int r = real ? min(r0 + 8 * wave + (lane >> 3), last) : 0;
+  return dense ? prow[r >> 5] + (uint32_t)(r & (MLA_T - 1)) : prow[r] & ~INVALID_ROW;
 }
 template <bool WIDE>
 __device__ __forceinline__ void issue_part(const __amdgpu_buffer_rsrc_t rs, const uint16_t *__restrict__ kv,
@@ -185,8 +189,8 @@ __device__ __forceinline__ void issue_part(const __amdgpu_buffer_rsrc_t rs, cons
 template <bool WIDE>
 __device__ __forceinline__ void issue_tile(const __amdgpu_buffer_rsrc_t rs, const uint16_t *__restrict__ kv,
                                            uint32_t brow, const uint32_t *prow, int r0, bool real, int last,
-                                           uint8_t *buf, int wave, int lane) {
-  const uint32_t row = tile_row(prow, r0, real, last, wave, lane);
+                                           bool dense, uint8_t *buf, int wave, int lane) {
+  const uint32_t row = tile_row(prow, r0, real, last, dense, wave, lane);
 #pragma unroll
   for (int i = 0; i < LOADS_PER_WAVE; ++i) issue_part<WIDE>(rs, kv, brow, row, buf, wave, lane, i);
 }
@@ -261,14 +265,39 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
   // Selected positions -> physical rows.  A position outside [0, n_vis) breaks
   // the contract; it is loaded from position 0 (in bounds, finite) and masked.
   const int seq = a.q_seq[q];
-  const int32_t *ip = a.idx + (int64_t)q * a.k + r0;
   // All of a thread's positions, and then their block-table entries, are
   // loaded before any is used, every lane issuing the same loads (indices
   // clamped into range, no branch), so they overlap instead of taking one
   // memory latency per row.
   constexpr int PER_THREAD = MLA_MAX_ROWS / MLA_THREADS;
+  constexpr int PER_THREAD_T = (MLA_MAX_ROWS + MLA_T + MLA_THREADS - 1) / MLA_THREADS;
+  const bool dense = p.dense != 0;
   int bad = 0;
-  if (nrows > 0) {  // block-uniform
+  if (dense && nrows > 0) {  // block-uniform
+    // Dense: the base row of each 32-row tile of positions r0, r0 + 32, ...
+    const int nt = (nrows + MLA_T - 1) / MLA_T;  // <= MLA_MAX_ROWS + MLA_T (the launcher splits longer rows)
+    uint32_t base[PER_THREAD_T];
+    if (a.map.block_shift < 0) {
+      const uint32_t s0 = (uint32_t)a.map.seq_row0[seq] + (uint32_t)r0;
+#pragma unroll
+      for (int j = 0; j < PER_THREAD_T; ++j) base[j] = s0 + (uint32_t)(MLA_T * (tid + j * MLA_THREADS));
+    } else {
+      const int32_t *bt = a.map.block_table + (int64_t)seq * a.map.max_blocks;
+      const int sh = a.map.block_shift;
+      int32_t blk[PER_THREAD_T];
+#pragma unroll
+      for (int j = 0; j < PER_THREAD_T; ++j) blk[j] = bt[(r0 + MLA_T * min(tid + j * MLA_THREADS, nt - 1)) >> sh];
+#pragma unroll
+      for (int j = 0; j < PER_THREAD_T; ++j) {
+        const int pos = r0 + MLA_T * min(tid + j * MLA_THREADS, nt - 1);
+        base[j] = ((uint32_t)blk[j] << sh) + (uint32_t)(pos & ((1 << sh) - 1));
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < PER_THREAD_T; ++j)
+      if (tid + j * MLA_THREADS < nt) prow[tid + j * MLA_THREADS] = base[j];
+  } else if (nrows > 0) {  // block-uniform
+    const int32_t *ip = a.idx + (int64_t)q * a.k + r0;
     int pos[PER_THREAD];
 #pragma unroll
     for (int j = 0; j < PER_THREAD; ++j) pos[j] = ip[min(tid + j * MLA_THREADS, nrows - 1)];
@@ -345,8 +374,8 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
       (!WIDE && a.map.block_shift < 0) ? (uint32_t)a.map.seq_row0[seq] : 0u);
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t *>(a.kv + (size_t)brow * 576), (short)0, 0xFFFFFFFF, 0x00020000);
-  if (ntiles > 0) issue_tile<WIDE>(rs, a.kv, brow, prow, 0, true, nrows - 1, tb0, wave, lane);
-  if (!PIPE && ntiles > 1) issue_tile<WIDE>(rs, a.kv, brow, prow, MLA_T, true, nrows - 1, tb1, wave, lane);
+  if (ntiles > 0) issue_tile<WIDE>(rs, a.kv, brow, prow, 0, true, nrows - 1, dense, tb0, wave, lane);
+  if (!PIPE && ntiles > 1) issue_tile<WIDE>(rs, a.kv, brow, prow, MLA_T, true, nrows - 1, dense, tb1, wave, lane);
   // Queries of this wavefront's own 32 heads: B fragments of S^T = K . Q^T,
   // loaded while the first two tiles are gathered.
   uint4 qb[36];
@@ -406,11 +435,12 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int rbase = t0 + 8 * i + 4 * g;
-        const uint4 pr = *reinterpret_cast<const uint4 *>(&prow[rbase]);
+        // (Dense: prow holds tile bases, and every row below nrows is valid.)
+        const uint4 pr = dense ? make_uint4(0u, 0u, 0u, 0u) : *reinterpret_cast<const uint4 *>(&prow[rbase]);
         const uint32_t prv[4] = {pr.x, pr.y, pr.z, pr.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const bool ok = (rbase + j < nrows) && !(prv[j] & INVALID_ROW);
+          const bool ok = (rbase + j < nrows) && (dense || !(prv[j] & INVALID_ROW));
           const float v = ok ? s[4 * i + j] * p.scale_log2 : -INFINITY;
           z[4 * i + j] = v;
           tmax = fmaxf(tmax, v);
@@ -532,7 +562,8 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
       // (no branch between the MFMAs, which would make the compiler drain the
       // LDS read ring), but all read one row of this block, which stays in
       // cache, into the free buffer.
-      issue_tile<WIDE>(rs, a.kv, brow, prow, t * MLA_T + 2 * MLA_T, t + 2 < ntiles, nrows - 1, nbuf, wave, lane);
+      issue_tile<WIDE>(rs, a.kv, brow, prow, t * MLA_T + 2 * MLA_T, t + 2 < ntiles, nrows - 1, dense, nbuf, wave,
+                       lane);
       __builtin_amdgcn_sched_barrier(0);
       v16f s;
       qk(buf, s, no_hook);
@@ -579,7 +610,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
       constexpr bool PREV = decltype(prev)::value;
       wait_tile(t);
       // Past the last tile the parts read one cached row into the free buffer.
-      const uint32_t nrow = tile_row(prow, (t + 1) * MLA_T, t + 1 < ntiles, nrows - 1, wave, lane);
+      const uint32_t nrow = tile_row(prow, (t + 1) * MLA_T, t + 1 < ntiles, nrows - 1, dense, wave, lane);
       v16f s;
       qk(buf, s, [&](const int ks) {
         if (ks < LOADS_PER_WAVE) issue_part<WIDE>(rs, a.kv, brow, nrow, nbuf, wave, lane, ks);
@@ -728,8 +759,15 @@ static int rows_per_split(int k, int nsplit) {
   return (r + MLA_T - 1) / MLA_T * MLA_T;
 }
 
-size_t mla_ws_bytes(int num_q, int k, bool decode) {
-  const int ns = mla_num_splits(num_q, k, decode);
+int mla_dense_splits(int num_q, int max_nvis) {
+  const int64_t max_rows = (int64_t)(MLA_MAX_ROWS + MLA_T) * MLA_T;  // tiles per workgroup x 32 rows
+  const int least = (int)((max_nvis + max_rows - 1) / max_rows);
+  const int ns = mla_num_splits(num_q, max_nvis, true);
+  return ns > least ? ns : (least > 0 ? least : 1);
+}
+
+size_t mla_ws_bytes(int num_q, int k, bool decode, bool dense) {
+  const int ns = dense ? mla_dense_splits(num_q, k) : mla_num_splits(num_q, k, decode);
   if (ns <= 1) return 0;
   return (size_t)num_q * ns * 128 * (512 + 1) * sizeof(float) + 256;
 }
@@ -738,7 +776,8 @@ hipError_t launch_mla(const MlaLaunch &a, bool decode, void *ws, hipStream_t st)
   if (a.num_q == 0) return hipSuccess;
   MlaKernelArgs p;
   p.a = a;
-  p.nsplit = mla_num_splits(a.num_q, a.k, decode);
+  p.nsplit = a.dense ? mla_dense_splits(a.num_q, a.k) : mla_num_splits(a.num_q, a.k, decode);
+  p.dense = a.dense ? 1 : 0;
   p.rows_per_split = rows_per_split(a.k, p.nsplit);
   p.scale_log2 = a.softmax_scale * LOG2E;
   p.part_o = nullptr;

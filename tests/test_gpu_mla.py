@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import sparse_long_context_dsa_amd as dsa
 from gpu_util import OracleView, banner, bf16_bits, check_out
 from workloads import make_custom
@@ -175,3 +176,72 @@ def test_paged_pool_beyond_4gib(decode):
     compare(wl, idx, cnt, 2048, decode)
     del kv
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------ dense mode
+
+
+def run_dense(wl):
+    q = dsa.Queries(wl.q_seq, wl.q_nvis, wl.max_nvis)
+    if wl.block_size:
+        lay = dsa.KvLayout(wl.num_seqs, wl.rows, block_table=wl.block_table, block_size=wl.block_size)
+    else:
+        lay = dsa.KvLayout(wl.num_seqs, wl.rows, seq_row0=wl.row0)
+    out = torch.full((wl.nq, 128, 512), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full((wl.nq, 128), float("nan"), dtype=torch.float32, device="cuda")
+    dsa.dsa_dense_mla(q, lay, wl.q_mla, wl.kv, wl.softmax_scale, out, lse)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), lse.cpu().numpy()
+
+
+def check_dense(wl, queries):
+    out, lse = run_dense(wl)
+    ov = OracleView(wl)
+    for i in queries:
+        r = ov.rows(i)
+        kv = bf16_bits(wl.kv[torch.from_numpy(r).cuda()]) if r.size else np.zeros((0, 576), np.uint16)
+        o_ref, l_ref = oracle.dense_mla(bf16_bits(wl.q_mla[i]), kv, wl.softmax_scale)
+        check_out(out[i], o_ref, lse[i], l_ref, f"dense {wl.name} q{i}")
+    return out, lse
+
+
+@pytest.mark.parametrize("paged,block", [(False, 64), (True, 64), (True, 256)])
+def test_dense_decode_against_oracle(paged, block):
+    """Every visible position, one query per sequence: histories around tile
+    and split boundaries, contiguous and paged caches (oracle: the separately
+    written dense attention)."""
+    banner(f"dense mla decode paged={paged} block={block}")
+    wl = make_custom(seq_lens=[0, 1, 31, 33, 2048, 5000, 20000], device="cuda", seed=51, paged=paged,
+                     block_size=block)
+    out, lse = check_dense(wl, range(1, wl.nq))
+    assert (out[0] == 0).all() and np.isneginf(lse[0]).all()
+
+
+def test_dense_prefill_causal():
+    banner("dense mla prefill")
+    wl = make_custom(seq_lens=[3000], device="cuda", seed=52, prefill=True, queries_per_seq=300)
+    check_dense(wl, [0, 1, 150, 298, 299])
+
+
+def test_dense_history_longer_than_one_workgroup_holds():
+    """70000 positions: more tiles than one workgroup's row table, so the
+    launch must split the rows even for a single query."""
+    banner("dense mla 70000 positions")
+    wl = make_custom(seq_lens=[70000], device="cuda", seed=53)
+    check_dense(wl, [0])
+
+
+def test_dense_equals_sparse_over_all_positions_bit_exact():
+    """With one workgroup per query (many queries), the dense mode and the
+    sparse prefill given idx = 0 .. n-1 gather the same tiles in the same order:
+    the outputs must agree bit for bit."""
+    banner("dense vs sparse over every position")
+    wl = make_custom(seq_lens=[2048] * 4, device="cuda", seed=54, prefill=True, queries_per_seq=150)
+    out_d, lse_d = run_dense(wl)
+    nv = wl.q_nvis.cpu().numpy()
+    idx = np.full((wl.nq, 2048), -1, np.int32)
+    for i in range(wl.nq):
+        idx[i, :nv[i]] = np.arange(nv[i])
+    out_s, lse_s = run_mla(wl, idx, np.minimum(nv, 2048).astype(np.int32), 2048, False)
+    assert (out_d.view(np.uint32) == out_s.view(np.uint32)).all()
+    assert (lse_d.view(np.uint32) == lse_s.view(np.uint32)).all()
