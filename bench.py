@@ -337,12 +337,52 @@ def decode_result(args):
     return result
 
 
+def crossover_result(args):
+    """Sparse path (dsa_forward: indexer, top-k, attention over k rows) against
+    the dense mode (dsa_dense_mla over the whole history) on decode batches of
+    64 queries, as the history grows.  Each side: `warmup` untimed calls, then
+    `steps` timed ones between two synchronizes."""
+    import sparse_long_context_dsa_amd as dsa
+    from workloads import make_custom
+    rows = []
+    for L in (1024, 2048, 2560, 3072, 4096, 6144, 8192, 16384, 32768):
+        log(f"crossover: context {L}")
+        wl = make_custom(seq_lens=[L] * 64, device="cuda", seed=70 + L % 97, plant=True)
+        p = prepare(wl)
+        wall, _, _ = time_forward(wl, p, args.steps, args.warmup)
+        dws = dsa.workspace(dsa.DSA_OP_MLA_DENSE, p["queries"], 1)
+
+        def dense():
+            dsa.dsa_dense_mla(p["queries"], p["layout"], wl.q_mla, wl.kv, wl.softmax_scale, p["out"], p["lse"],
+                              ws=dws)
+
+        for _ in range(args.warmup):
+            dense()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            dense()
+        torch.cuda.synchronize()
+        dwall = time.perf_counter() - t0
+        rows.append({"context": L, "sparse_ms": 1e3 * wall / args.steps, "dense_ms": 1e3 * dwall / args.steps})
+        del p, wl, dws
+        torch.cuda.empty_cache()
+    cross = next((r["context"] for r in rows if r["sparse_ms"] < r["dense_ms"]), None)
+    result = {"metric": "shortest decode history where the sparse path beats dense attention (batch 64, k=2048)",
+              "value": cross, "unit": "positions"}
+    result.update(common_fields(args))
+    result.update({"higher_is_better": False,
+                   "config": {"workload": "decode 64 x L, L from 1024 to 32768", "batch": 64, "k": 2048},
+                   "rows": rows})
+    return result
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", choices=("decode", "prefill"), default="decode")
+    ap.add_argument("--workload", choices=("decode", "prefill", "crossover"), default="decode")
     ap.add_argument("--cpu-sample", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
@@ -358,7 +398,9 @@ def main():
     import sparse_long_context_dsa_amd as dsa
     dsa._lib.lib()  # fail loudly if the HIP library is missing
     log(f"library {dsa.lib_path()}")
-    if args.workload == "prefill":
+    if args.workload == "crossover":
+        result = crossover_result(args)
+    elif args.workload == "prefill":
         result = prefill_result(args)
         if args.copy_calib:
             log("calibration copy")
