@@ -16,12 +16,15 @@ function is that definition written out:
 * ``layout``   - logical position -> physical cache row (contiguous or paged).
 * ``dsa``      - lightning-indexer scores, top-k selection, sparse and dense
                  MQA-mode MLA attention, and their composition.
+* ``kl``       - the indexer's training loss: the head-summed attention target,
+                 KL(target || Softmax(I)) and the gradients with respect to the
+                 indexer's scores and inputs.
 
 Sources are the web pages on DeepSeek Sparse Attention; each function names the
 page and the section or equation it follows.
 """
 
-from . import bf16, dsa, fp8, layout  # noqa: F401
+from . import bf16, dsa, fp8, kl, layout  # noqa: F401
 from .bf16 import bf16_decode  # noqa: F401
 from .dsa import (  # noqa: F401
     dense_mla,
@@ -32,4 +35,12 @@ from .dsa import (  # noqa: F401
     topk,
 )
 from .fp8 import E4M3_MAX, e4m3_decode, e4m3_encode, e8m0_decode, quantize_rows, quantize_rows_e8m0  # noqa: F401
+from .kl import (  # noqa: F401
+    attention_target,
+    dequantise,
+    indexer_backward_query,
+    indexer_kl_query,
+    indexer_logits,
+    kl_to_softmax,
+)
 from .layout import phys_rows  # noqa: F401
