@@ -210,6 +210,42 @@ int dsa_sparse_mla_prefill(const dsa_queries *queries, const dsa_kv_layout *layo
                            float *out, float *lse, void *ws, size_t ws_bytes,
                            hipStream_t stream);
 
+/* Indexer alignment loss, sparse training stage (page "arXiv'25 | DSA ...",
+ * section 5.2, L_I over the selected set S_t; the mlpod.com page on
+ * DeepSeek-V3.2-Exp, part 2.1.2).  For each query the target p is the
+ * attention's probabilities over the set summed over the 128 heads and
+ * L1-normalised over the set; the loss term is KL(p || Softmax(I)) over the
+ * same set, and the gradient with respect to the indexer scores is
+ * Softmax(I) - p (p is a constant: the indexer's inputs are detached).
+ *   q, kv, idx, count, k : the attention's inputs, as for dsa_sparse_mla_decode
+ *           (entries of idx outside [0, q_nvis[i]) are not in the set);
+ *   lse    : fp32 [num_q, 128], the natural-log log-sum-exp that the attention
+ *           over the same set returned (the probabilities are recomputed from
+ *           q, kv and lse; a head whose lse is not finite contributes 0);
+ *   scores : fp32 [num_q, ld_scores], the indexer's I by position; it must hold
+ *           every position of the set (the short-history bypass of dsa_forward
+ *           does not score, so training calls dsa_indexer_scores for all);
+ *   grad   : fp32 [num_q, k] dL/dI in set order (entry j belongs to idx[i, j];
+ *           0 past count and for entries not in the set);
+ *   target : fp32 [num_q, k] p in the same order, or NULL;
+ *   kl     : fp32 [num_q] the per-query terms; loss : fp32 [1] their sum, or NULL.
+ * An empty set gives kl = 0.  No workspace; deterministic. */
+int dsa_indexer_kl_sparse(const dsa_queries *queries, const dsa_kv_layout *layout,
+                          const uint16_t *q, const uint16_t *kv, const int32_t *idx,
+                          const int32_t *count, int32_t k, const float *lse,
+                          float softmax_scale, const float *scores, int64_t ld_scores,
+                          float *grad, float *target, float *kl, float *loss,
+                          hipStream_t stream);
+/* Dense warm-up stage (page "arXiv'25 | DSA ...", section 5.1, L_I over every
+ * visible position; the mlpod.com page, part 2.1.1): the same loss with the set
+ * = [0, q_nvis[i]) and lse from dsa_dense_mla.  grad and target (or NULL) are
+ * fp32 [num_q, ld_grad] by position, written for s < q_nvis[i]. */
+int dsa_indexer_kl_dense(const dsa_queries *queries, const dsa_kv_layout *layout,
+                         const uint16_t *q, const uint16_t *kv, const float *lse,
+                         float softmax_scale, const float *scores, int64_t ld_scores,
+                         float *grad, float *target, int64_t ld_grad, float *kl,
+                         float *loss, hipStream_t stream);
+
 /* The whole layer hot path: indexer -> top-k -> sparse attention (page
  * "DeepSeekV3.2之DSA", part 5.1 decode data flow), with the short-history
  * bypass of part 4.5 (a query with q_nvis <= k is not scored and attends to

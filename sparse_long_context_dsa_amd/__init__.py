@@ -22,7 +22,8 @@ from ._lib import (  # noqa: F401
 __all__ = [
     "HipEvents", "Queries", "KvLayout", "dsa_quantize_fp8", "dsa_quantize_fp8_e8m0", "dsa_indexer_scores",
     "dsa_indexer_scores_e8m0", "dsa_topk",
-    "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill", "dsa_dense_mla", "dsa_forward", "dsa_workspace_bytes",
+    "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill", "dsa_dense_mla", "dsa_indexer_kl_sparse",
+    "dsa_indexer_kl_dense", "dsa_forward", "dsa_workspace_bytes",
     "workspace", "lib_path",
 ]
 
@@ -220,6 +221,52 @@ def dsa_dense_mla(queries, layout, q, kv, softmax_scale, out, lse=None, ws=None,
         ctypes.byref(qc), ctypes.byref(lc), _ptr(q), _ptr(kv), float(softmax_scale), _ptr(out), _ptr(lse),
         _ptr(ws), ws.numel(), _stream(stream)))
     return ws
+
+
+def dsa_indexer_kl_sparse(queries, layout, q, kv, idx, count, k, lse, softmax_scale, scores, grad, kl,
+                          target=None, loss=None, stream=None):
+    """Indexer KL loss over each query's selected set: grad [num_q, k] = dL/dI in
+    set order, kl [num_q], optional target [num_q, k] and loss [1]."""
+    nq = queries.num_q
+    _need(q, torch.bfloat16, (nq, DSA_H, DSA_D), "q")
+    _need(kv, torch.bfloat16, (layout.num_rows, DSA_D), "kv")
+    _need(idx, torch.int32, (nq, k), "idx")
+    if count is not None:
+        _need(count, torch.int32, (nq,), "count")
+    _need(lse, torch.float32, (nq, DSA_H), "lse")
+    _need(scores, torch.float32, None, "scores")
+    _need(grad, torch.float32, (nq, k), "grad")
+    _need(kl, torch.float32, (nq,), "kl")
+    if target is not None:
+        _need(target, torch.float32, (nq, k), "target")
+    if loss is not None:
+        _need(loss, torch.float32, (1,), "loss")
+    qc, lc = queries.c(), layout.c()
+    _lib.check("dsa_indexer_kl_sparse", _lib.lib().dsa_indexer_kl_sparse(
+        ctypes.byref(qc), ctypes.byref(lc), _ptr(q), _ptr(kv), _ptr(idx), _ptr(count), k, _ptr(lse),
+        float(softmax_scale), _ptr(scores), scores.shape[-1], _ptr(grad), _ptr(target), _ptr(kl), _ptr(loss),
+        _stream(stream)))
+
+
+def dsa_indexer_kl_dense(queries, layout, q, kv, lse, softmax_scale, scores, grad, kl, target=None, loss=None,
+                         stream=None):
+    """Indexer KL loss over every visible position: grad [num_q, ld] = dL/dI by
+    position (s < q_nvis), kl [num_q], optional target (like grad) and loss [1]."""
+    nq = queries.num_q
+    _need(q, torch.bfloat16, (nq, DSA_H, DSA_D), "q")
+    _need(kv, torch.bfloat16, (layout.num_rows, DSA_D), "kv")
+    _need(lse, torch.float32, (nq, DSA_H), "lse")
+    _need(scores, torch.float32, None, "scores")
+    _need(grad, torch.float32, None, "grad")
+    _need(kl, torch.float32, (nq,), "kl")
+    if target is not None:
+        _need(target, torch.float32, tuple(grad.shape), "target")
+    if loss is not None:
+        _need(loss, torch.float32, (1,), "loss")
+    qc, lc = queries.c(), layout.c()
+    _lib.check("dsa_indexer_kl_dense", _lib.lib().dsa_indexer_kl_dense(
+        ctypes.byref(qc), ctypes.byref(lc), _ptr(q), _ptr(kv), _ptr(lse), float(softmax_scale), _ptr(scores),
+        scores.shape[-1], _ptr(grad), _ptr(target), grad.shape[-1], _ptr(kl), _ptr(loss), _stream(stream)))
 
 
 def dsa_forward(queries: Queries, layout: KvLayout, q_fp8, q_scale, w, k_fp8, k_scale, q, kv, k,

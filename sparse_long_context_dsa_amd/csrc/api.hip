@@ -1,6 +1,6 @@
 // C ABI of libdsa.so: argument checks on the host, workspace carving, and the
-// stream-ordered launches of the kernels in indexer.hip, topk.hip, mla.hip and
-// quant.hip.  Nothing here allocates device memory or synchronises.
+// stream-ordered launches of the kernels in indexer.hip, topk.hip, mla.hip,
+// kl.hip and quant.hip.  Nothing here allocates device memory or synchronises.
 #include <cstdarg>
 #include <climits>
 #include <cstdio>
@@ -246,6 +246,48 @@ int dsa_dense_mla(const dsa_queries *qr, const dsa_kv_layout *ly, const uint16_t
   dsa::MlaLaunch a{q, kv, nullptr, nullptr, qr->q_seq, qr->q_nvis, m, longest, qr->num_q, softmax_scale, out, lse,
                    ly->num_rows, true};
   return hip_status(dsa::launch_mla(a, true, ws, stream), "dense MLA launch");
+}
+
+static int kl_impl(const dsa_queries *qr, const dsa_kv_layout *ly, const uint16_t *q, const uint16_t *kv,
+                   const int32_t *idx, const int32_t *count, int32_t k, const float *lse, float softmax_scale,
+                   const float *scores, int64_t ld_scores, float *grad, float *target, int64_t ld_grad, float *kl,
+                   float *loss, hipStream_t stream) {
+  int st;
+  if ((st = check_queries(qr))) return st;
+  const bool sparse = idx != nullptr;
+  if (sparse && (st = check_k(k))) return st;
+  dsa::KvMap m;
+  if ((st = check_layout(ly, m))) return st;
+  if (qr->num_q > 0) {
+    if (!q || !kv || !lse || !scores || !grad || !kl)
+      return fail(DSA_ERR_INVALID_ARG, "q, kv, lse, scores, grad and kl must be non-NULL");
+    if (!aligned(q, 16) || !aligned(kv, 16)) return fail(DSA_ERR_INVALID_ARG, "q and kv must be 16-byte aligned");
+    if (ld_scores < qr->max_nvis)
+      return fail(DSA_ERR_INVALID_ARG, "ld_scores = %lld < max_nvis = %d", (long long)ld_scores, qr->max_nvis);
+    if (!sparse && ld_grad < qr->max_nvis)
+      return fail(DSA_ERR_INVALID_ARG, "ld_grad = %lld < max_nvis = %d", (long long)ld_grad, qr->max_nvis);
+  }
+  if (qr->num_q == 0 && !loss) return ok();
+  const int max_set = sparse ? (qr->max_nvis < k ? qr->max_nvis : k) : qr->max_nvis;
+  dsa::KlLaunch a{q, kv, idx, count, qr->q_seq, qr->q_nvis, m, lse, scores, ld_scores, sparse ? k : 0, qr->num_q,
+                  softmax_scale, ly->num_rows, grad, sparse ? (int64_t)k : ld_grad, target, kl, loss};
+  return hip_status(dsa::launch_indexer_kl(a, max_set, stream), "indexer KL launch");
+}
+
+int dsa_indexer_kl_sparse(const dsa_queries *qr, const dsa_kv_layout *ly, const uint16_t *q, const uint16_t *kv,
+                          const int32_t *idx, const int32_t *count, int32_t k, const float *lse,
+                          float softmax_scale, const float *scores, int64_t ld_scores, float *grad, float *target,
+                          float *kl, float *loss, hipStream_t stream) {
+  if (qr && qr->num_q > 0 && !idx) return fail(DSA_ERR_INVALID_ARG, "idx must be non-NULL");
+  return kl_impl(qr, ly, q, kv, idx, count, k, lse, softmax_scale, scores, ld_scores, grad, target, k, kl, loss,
+                 stream);
+}
+
+int dsa_indexer_kl_dense(const dsa_queries *qr, const dsa_kv_layout *ly, const uint16_t *q, const uint16_t *kv,
+                         const float *lse, float softmax_scale, const float *scores, int64_t ld_scores, float *grad,
+                         float *target, int64_t ld_grad, float *kl, float *loss, hipStream_t stream) {
+  return kl_impl(qr, ly, q, kv, nullptr, nullptr, 0, lse, softmax_scale, scores, ld_scores, grad, target, ld_grad,
+                 kl, loss, stream);
 }
 
 static int forward_impl(const dsa_queries *qr, const dsa_kv_layout *ly, const uint8_t *q_fp8, const float *q_scale,

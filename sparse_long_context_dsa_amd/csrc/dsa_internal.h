@@ -101,4 +101,31 @@ int mla_dense_splits(int num_q, int max_nvis);
 size_t mla_ws_bytes(int num_q, int k, bool decode, bool dense = false);
 hipError_t launch_mla(const MlaLaunch &a, bool decode, void *ws, hipStream_t st);
 
+// Indexer alignment loss: target a[r] = sum_h exp(z[h, r] - lse[h]) over each
+// query's set (written into grad), then KL(a / |a|_1 || Softmax(I)) per query
+// and its gradient (overwriting grad), and the sum over the queries.
+struct KlLaunch {
+  const uint16_t *q;
+  const uint16_t *kv;
+  const int32_t *idx;    // sparse: [num_q, k] set positions; null: every visible position
+  const int32_t *count;  // may be null
+  const int32_t *q_seq;
+  const int32_t *q_nvis;
+  KvMap map;
+  const float *lse;      // [num_q, 128] the attention's log-sum-exp over the same set
+  const float *scores;   // [num_q, ld_scores] indexer scores by position
+  int64_t ld_scores;
+  int32_t k;             // sparse: the idx row length
+  int32_t num_q;
+  float softmax_scale;
+  int64_t num_rows;      // rows of the latent cache
+  float *grad;           // [num_q, ld_out]: sparse in set order (ld_out = k), dense by position
+  int64_t ld_out;
+  float *target;         // may be null; same layout as grad
+  float *kl;             // [num_q]
+  float *loss;           // may be null
+};
+// max_set: the largest set (sparse: min(k, longest history); dense: the longest history).
+hipError_t launch_indexer_kl(const KlLaunch &a, int max_set, hipStream_t st);
+
 }  // namespace dsa
