@@ -377,12 +377,106 @@ def crossover_result(args):
     return result
 
 
+def kl_result(args):
+    """The indexer's KL loss on the 16384-token causal prefill (the training
+    shape): the sparse stage over each query's top-k set (from dsa_forward,
+    with the attention's lse) and the dense warm-up over every visible
+    position (lse from dsa_dense_mla).  Indexer scores for every position come
+    from dsa_indexer_scores.  Each call: `warmup` untimed, then `steps` timed
+    between two synchronizes.  The dominant kernel recomputes the attention
+    logits (128 heads x 576 x 2 flop per member of a set) on bf16 MFMA; its rate
+    is quoted over the whole call (target, loss and sum kernels), so it is a
+    lower bound on the target kernel's own."""
+    import oracle
+    import sparse_long_context_dsa_amd as dsa
+    from workloads import make_config
+    log("kl: generating the 16384-token causal workload")
+    wl = make_config(3, device="cuda")
+    p = prepare(wl)
+    nq = wl.nq
+    dsa.dsa_forward(p["queries"], p["layout"], p["q8"], p["qs"], wl.w, p["k8"], p["ks"], wl.q_mla, wl.kv, wl.k,
+                    wl.softmax_scale, p["out"], p["lse"], p["idx"], ws=p["ws"])
+    ld = (wl.max_nvis + 63) // 64 * 64
+    scores = torch.empty((nq, ld), dtype=torch.float32, device="cuda")
+    dsa.dsa_indexer_scores(p["queries"], p["layout"], p["q8"], p["qs"], wl.w, p["k8"], p["ks"], scores)
+    kl = torch.empty((nq,), dtype=torch.float32, device="cuda")
+    loss = torch.empty((1,), dtype=torch.float32, device="cuda")
+    grad_s = torch.empty((nq, wl.k), dtype=torch.float32, device="cuda")
+    nv = wl.q_nvis.cpu().numpy()
+    members_s = int(np.minimum(nv, wl.k).sum())
+    members_d = int(nv.sum())
+
+    def timed(call):
+        for _ in range(args.warmup):
+            call()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            call()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / args.steps
+
+    log("kl: sparse stage")
+    t_s = timed(lambda: dsa.dsa_indexer_kl_sparse(p["queries"], p["layout"], wl.q_mla, wl.kv, p["idx"], None, wl.k,
+                                                  p["lse"], wl.softmax_scale, scores, grad_s, kl, loss=loss))
+    loss_s = float(loss.item())
+    del grad_s
+    log("kl: dense warm-up")
+    lse_d = torch.empty((nq, 128), dtype=torch.float32, device="cuda")
+    dws = dsa.workspace(dsa.DSA_OP_MLA_DENSE, p["queries"], 1)
+    dsa.dsa_dense_mla(p["queries"], p["layout"], wl.q_mla, wl.kv, wl.softmax_scale, p["out"], lse_d, ws=dws)
+    grad_d = torch.empty((nq, ld), dtype=torch.float32, device="cuda")
+    t_d = timed(lambda: dsa.dsa_indexer_kl_dense(p["queries"], p["layout"], wl.q_mla, wl.kv, lse_d, wl.softmax_scale,
+                                                 scores, grad_d, kl, loss=loss))
+    loss_d = float(loss.item())
+    flop_member = 128 * 576 * 2
+    tf_s = members_s * flop_member / t_s / 1e12
+    tf_d = members_d * flop_member / t_d / 1e12
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("kl: timing the CPU oracle on a bounded sample")
+        idx_h = p["idx"].cpu().numpy()
+        sc_h = scores.cpu().numpy()
+        sample = [int(i) for i in np.linspace(nq - 64, nq - 1, 16)]
+        inputs = []
+        for i in sample:
+            c = int(min(nv[i], wl.k))
+            pos = idx_h[i, :c]
+            rows = int(wl.row0[0].item()) + pos
+            kvr = wl.kv[torch.from_numpy(rows).cuda()].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+            qm = wl.q_mla[i].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+            inputs.append((qm, kvr, sc_h[i, pos].astype(np.float64)))
+        t0 = time.perf_counter()
+        for qm, kvr, x in inputs:
+            oracle.indexer_kl_query(qm, kvr, x, wl.softmax_scale)
+        dt = time.perf_counter() - t0
+        cpu = {"value": len(sample) / dt, "unit": "queries/s", "cores": len(os.sched_getaffinity(0)),
+               "kind": "oracle", "sample": f"{len(sample)} of the last 64 queries (2048-member sets), sparse stage, "
+                                           f"{dt:.2f} s"}
+    result = {"metric": "indexer KL loss, sparse stage: queries/s (16384-token causal prefill, k=2048)",
+              "value": nq / t_s, "unit": "queries/s"}
+    result.update(common_fields(args))
+    result.update({
+        "dtype": "bf16", "ms_per_step": 1e3 * t_s,
+        "config": {"workload": "prefill 16384 tokens, causal, k=2048: indexer KL loss", "tokens": nq, "k": wl.k,
+                   "heads": 128, "latent": 576},
+        "roofline": {"bound": "mfma", "kernel": "kl_target", "achieved": tf_s, "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": tf_s / BF16_PEAK_TFLOPS, "traffic": None},
+        "sparse": {"members": members_s, "ms": 1e3 * t_s, "tflops_bf16": tf_s, "loss": loss_s},
+        "dense_warmup": {"members": members_d, "ms": 1e3 * t_d, "tflops_bf16": tf_d,
+                         "frac_bf16_peak": tf_d / BF16_PEAK_TFLOPS, "loss": loss_d},
+    })
+    if cpu:
+        result["cpu_baseline"] = cpu
+    return result
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", choices=("decode", "prefill", "crossover"), default="decode")
+    ap.add_argument("--workload", choices=("decode", "prefill", "crossover", "kl"), default="decode")
     ap.add_argument("--cpu-sample", type=int, default=16)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
@@ -400,6 +494,8 @@ def main():
     log(f"library {dsa.lib_path()}")
     if args.workload == "crossover":
         result = crossover_result(args)
+    elif args.workload == "kl":
+        result = kl_result(args)
     elif args.workload == "prefill":
         result = prefill_result(args)
         if args.copy_calib:
