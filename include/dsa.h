@@ -246,6 +246,37 @@ int dsa_indexer_kl_dense(const dsa_queries *queries, const dsa_kv_layout *layout
                          float *grad, float *target, int64_t ld_grad, float *kl,
                          float *loss, hipStream_t stream);
 
+/* Backward of the indexer score into its inputs (page "arXiv'25 | DSA ...",
+ * section 3, first equation I = sum_j w_j ReLU(q_j . k); section 5: only the
+ * indexer learns from its alignment loss, with its inputs detached from the
+ * main model).  Given grad = dL/dI over each query's set, the gradients with
+ * respect to the head weights and the dequantised FP8 query and key
+ * (q_scale * q8 and k_scale * k8: the quantiser passes gradients unchanged;
+ * the derivative of ReLU at exactly 0 is taken as 0):
+ *   dw[i,j]     = sum_s grad[i,s] ReLU(q_j . k_s)
+ *   dq[i,j,:]   = w[i,j] sum_s grad[i,s] [q_j . k_s > 0] k_s
+ *   dk[r(s),:] += grad[i,s] sum_j w[i,j] [q_j . k_s > 0] q_j
+ * (the sign of q_j . k_s is taken from the FP8 products summed in fp32).
+ *   q_fp8, q_scale, w, k_fp8, k_scale : as for dsa_indexer_scores;
+ *   idx, count, k : the set, as for dsa_indexer_kl_sparse; idx = NULL means
+ *            every visible position (dense warm-up; k and count unused);
+ *   grad   : fp32 dL/dI: [num_q, k] in set order when idx is given (as
+ *            dsa_indexer_kl_sparse writes it), else [num_q, ld_grad] by position;
+ *   dq     : fp32 [num_q, 64, 128], overwritten;
+ *   dw     : fp32 [num_q, 64], overwritten;
+ *   dk     : fp32 [R, 128], ADDED to (zero it first): a key row collects the
+ *            terms of every query whose set holds it.
+ * dk is summed with fp32 atomics, and so are dq and dw when a query's set is
+ * split over workgroups (sets of more than 2048 members, or small batches):
+ * there the rounding order, and so the last bits, can differ between runs.
+ * With one query per key row and one workgroup per query the result is
+ * deterministic.  No workspace. */
+int dsa_indexer_backward(const dsa_queries *queries, const dsa_kv_layout *layout,
+                         const uint8_t *q_fp8, const float *q_scale, const float *w,
+                         const uint8_t *k_fp8, const float *k_scale, const int32_t *idx,
+                         const int32_t *count, int32_t k, const float *grad, int64_t ld_grad,
+                         float *dq, float *dw, float *dk, hipStream_t stream);
+
 /* The whole layer hot path: indexer -> top-k -> sparse attention (page
  * "DeepSeekV3.2之DSA", part 5.1 decode data flow), with the short-history
  * bypass of part 4.5 (a query with q_nvis <= k is not scored and attends to

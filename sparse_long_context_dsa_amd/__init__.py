@@ -23,7 +23,7 @@ __all__ = [
     "HipEvents", "Queries", "KvLayout", "dsa_quantize_fp8", "dsa_quantize_fp8_e8m0", "dsa_indexer_scores",
     "dsa_indexer_scores_e8m0", "dsa_topk",
     "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill", "dsa_dense_mla", "dsa_indexer_kl_sparse",
-    "dsa_indexer_kl_dense", "dsa_forward", "dsa_workspace_bytes",
+    "dsa_indexer_kl_dense", "dsa_indexer_backward", "dsa_forward", "dsa_workspace_bytes",
     "workspace", "lib_path",
 ]
 
@@ -267,6 +267,37 @@ def dsa_indexer_kl_dense(queries, layout, q, kv, lse, softmax_scale, scores, gra
     _lib.check("dsa_indexer_kl_dense", _lib.lib().dsa_indexer_kl_dense(
         ctypes.byref(qc), ctypes.byref(lc), _ptr(q), _ptr(kv), _ptr(lse), float(softmax_scale), _ptr(scores),
         scores.shape[-1], _ptr(grad), _ptr(target), grad.shape[-1], _ptr(kl), _ptr(loss), _stream(stream)))
+
+
+def dsa_indexer_backward(queries, layout, q_fp8, q_scale, w, k_fp8, k_scale, idx, count, k, grad, dq, dw, dk,
+                         stream=None):
+    """Gradients of the indexer score with respect to w, the dequantised q and
+    the dequantised k, given grad = dL/dI over each query's set (idx [num_q, k]
+    with grad in set order, or idx None: every visible position, grad by
+    position).  dq [num_q, 64, 128] and dw [num_q, 64] are overwritten; dk
+    [rows, 128] is added to."""
+    nq = queries.num_q
+    _need(q_fp8, torch.uint8, (nq, DSA_HI, DSA_DI), "q_fp8")
+    if q_scale is not None:
+        _need(q_scale, torch.float32, (nq, DSA_HI), "q_scale")
+    _need(w, torch.float32, (nq, DSA_HI), "w")
+    _need(k_fp8, torch.uint8, (layout.num_rows, DSA_DI), "k_fp8")
+    _need(k_scale, torch.float32, (layout.num_rows,), "k_scale")
+    if idx is not None:
+        _need(idx, torch.int32, (nq, k), "idx")
+        _need(grad, torch.float32, (nq, k), "grad")
+    else:
+        _need(grad, torch.float32, None, "grad")
+        k = 0
+    if count is not None:
+        _need(count, torch.int32, (nq,), "count")
+    _need(dq, torch.float32, (nq, DSA_HI, DSA_DI), "dq")
+    _need(dw, torch.float32, (nq, DSA_HI), "dw")
+    _need(dk, torch.float32, (layout.num_rows, DSA_DI), "dk")
+    qc, lc = queries.c(), layout.c()
+    _lib.check("dsa_indexer_backward", _lib.lib().dsa_indexer_backward(
+        ctypes.byref(qc), ctypes.byref(lc), _ptr(q_fp8), _ptr(q_scale), _ptr(w), _ptr(k_fp8), _ptr(k_scale),
+        _ptr(idx), _ptr(count), k, _ptr(grad), grad.shape[-1], _ptr(dq), _ptr(dw), _ptr(dk), _stream(stream)))
 
 
 def dsa_forward(queries: Queries, layout: KvLayout, q_fp8, q_scale, w, k_fp8, k_scale, q, kv, k,

@@ -24,6 +24,7 @@ EXPORTED = (
     "dsa_dense_mla",
     "dsa_indexer_kl_sparse",
     "dsa_indexer_kl_dense",
+    "dsa_indexer_backward",
     "dsa_forward",
     "dsa_forward_profiled",
     "dsa_workspace_bytes",
@@ -85,6 +86,7 @@ def lib():
         "dsa_dense_mla": [qp, lp, vp, vp, f32, vp, vp, vp, sz, vp],
         "dsa_indexer_kl_sparse": [qp, lp, vp, vp, vp, vp, i32, vp, f32, vp, i64, vp, vp, vp, vp, vp],
         "dsa_indexer_kl_dense": [qp, lp, vp, vp, vp, f32, vp, i64, vp, vp, i64, vp, vp, vp],
+        "dsa_indexer_backward": [qp, lp, vp, vp, vp, vp, vp, vp, vp, i32, vp, i64, vp, vp, vp, vp],
         "dsa_forward": [qp, lp, vp, vp, vp, vp, vp, vp, vp, i32, f32, vp, vp, vp, vp, sz, vp],
         "dsa_forward_profiled": [qp, lp, vp, vp, vp, vp, vp, vp, vp, i32, f32, vp, vp, vp, vp, sz, vp, vp],
         "dsa_workspace_bytes": [ctypes.c_int, qp, i32],

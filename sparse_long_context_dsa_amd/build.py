@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdsa.so")
-SOURCES = ["api.hip", "indexer.hip", "topk.hip", "mla.hip", "kl.hip", "quant.hip"]
+SOURCES = ["api.hip", "indexer.hip", "indexer_bwd.hip", "topk.hip", "mla.hip", "kl.hip", "quant.hip"]
 ARCH = "gfx950"
 
 

@@ -1,6 +1,6 @@
 // C ABI of libdsa.so: argument checks on the host, workspace carving, and the
-// stream-ordered launches of the kernels in indexer.hip, topk.hip, mla.hip,
-// kl.hip and quant.hip.  Nothing here allocates device memory or synchronises.
+// stream-ordered launches of the kernels in indexer.hip, indexer_bwd.hip,
+// topk.hip, mla.hip, kl.hip and quant.hip.  Nothing here allocates device memory or synchronises.
 #include <cstdarg>
 #include <climits>
 #include <cstdio>
@@ -288,6 +288,32 @@ int dsa_indexer_kl_dense(const dsa_queries *qr, const dsa_kv_layout *ly, const u
                          float *target, int64_t ld_grad, float *kl, float *loss, hipStream_t stream) {
   return kl_impl(qr, ly, q, kv, nullptr, nullptr, 0, lse, softmax_scale, scores, ld_scores, grad, target, ld_grad,
                  kl, loss, stream);
+}
+
+int dsa_indexer_backward(const dsa_queries *qr, const dsa_kv_layout *ly, const uint8_t *q_fp8, const float *q_scale,
+                         const float *w, const uint8_t *k_fp8, const float *k_scale, const int32_t *idx,
+                         const int32_t *count, int32_t k, const float *grad, int64_t ld_grad, float *dq, float *dw,
+                         float *dk, hipStream_t stream) {
+  int st;
+  if ((st = check_queries(qr))) return st;
+  const bool sparse = idx != nullptr;
+  if (sparse && (st = check_k(k))) return st;
+  dsa::KvMap m;
+  if ((st = check_layout(ly, m))) return st;
+  if (qr->num_q == 0) return ok();
+  if (!q_fp8 || !w || !k_fp8 || !k_scale || !grad || !dq || !dw || !dk)
+    return fail(DSA_ERR_INVALID_ARG, "q_fp8, w, k_fp8, k_scale, grad, dq, dw and dk must be non-NULL");
+  if (!aligned(q_fp8, 16) || !aligned(k_fp8, 16))
+    return fail(DSA_ERR_INVALID_ARG, "q_fp8 and k_fp8 must be 16-byte aligned");
+  if (sparse) {
+    ld_grad = k;
+  } else if (ld_grad < qr->max_nvis) {
+    return fail(DSA_ERR_INVALID_ARG, "ld_grad = %lld < max_nvis = %d", (long long)ld_grad, qr->max_nvis);
+  }
+  const int max_set = sparse ? (qr->max_nvis < k ? qr->max_nvis : k) : qr->max_nvis;
+  dsa::IndexerBwdLaunch a{q_fp8, q_scale, w, k_fp8, k_scale, idx, count, qr->q_seq, qr->q_nvis, m,
+                          sparse ? k : 0, qr->num_q, grad, ld_grad, dq, dw, dk};
+  return hip_status(dsa::launch_indexer_bwd(a, max_set, stream), "indexer backward launch");
 }
 
 static int forward_impl(const dsa_queries *qr, const dsa_kv_layout *ly, const uint8_t *q_fp8, const float *q_scale,

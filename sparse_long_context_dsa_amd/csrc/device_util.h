@@ -22,6 +22,23 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// 16x16 FP8 (E4M3 x E4M3) product over K = 128 into fp32: lane l holds A row
+// l & 15 (B column l & 15) as the 32 bytes [32 (l >> 4), +32) of its K range;
+// the result's lane l holds column l & 15, rows 4 (l >> 4) .. + 3.
+__device__ __forceinline__ v4f mfma_fp8_16x16x128(const v8i &a, const v8i &b, const v4f &c) {
+  // Format 0 = FP8 E4M3 for both operands; E8M0 scale 127 = 2^0 (no scaling).
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0x7F7F7F7F, 0, 0x7F7F7F7F);
+}
+
+__device__ __forceinline__ v8i load32(const uint8_t *p) {
+  const uint4 x0 = *reinterpret_cast<const uint4 *>(p);
+  const uint4 x1 = *reinterpret_cast<const uint4 *>(p + 16);
+  v8i r;
+  r[0] = (int)x0.x; r[1] = (int)x0.y; r[2] = (int)x0.z; r[3] = (int)x0.w;
+  r[4] = (int)x1.x; r[5] = (int)x1.y; r[6] = (int)x1.z; r[7] = (int)x1.w;
+  return r;
+}
+
 // Value of v in lane l (l uniform across the wavefront).
 __device__ __forceinline__ int64_t readlane64(int64_t v, int l) {
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);

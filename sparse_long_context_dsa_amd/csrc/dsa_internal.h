@@ -128,4 +128,26 @@ struct KlLaunch {
 // max_set: the largest set (sparse: min(k, longest history); dense: the longest history).
 hipError_t launch_indexer_kl(const KlLaunch &a, int max_set, hipStream_t st);
 
+// Backward of the indexer score: dq, dw overwritten, dk accumulated (fp32 atomics).
+struct IndexerBwdLaunch {
+  const uint8_t *q8;     // [num_q, 64, 128]
+  const float *q_scale;  // [num_q, 64] or null (1)
+  const float *w;        // [num_q, 64]
+  const uint8_t *k8;     // [rows, 128]
+  const float *k_scale;  // [rows]
+  const int32_t *idx;    // sparse: [num_q, k]; null: every visible position
+  const int32_t *count;  // may be null
+  const int32_t *q_seq;
+  const int32_t *q_nvis;
+  KvMap map;
+  int32_t k;
+  int32_t num_q;
+  const float *grad;     // dL/dI: sparse [num_q, k] in set order, dense [num_q, ld_grad] by position
+  int64_t ld_grad;
+  float *dq;             // [num_q, 64, 128]
+  float *dw;             // [num_q, 64]
+  float *dk;             // [rows, 128], added to
+};
+hipError_t launch_indexer_bwd(const IndexerBwdLaunch &a, int max_set, hipStream_t st);
+
 }  // namespace dsa

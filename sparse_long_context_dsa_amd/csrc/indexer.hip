@@ -40,20 +40,6 @@ constexpr int IDX_KPW_MIN = 256;                 // keys per wavefront: a multip
 constexpr int IDX_KPW_MAX = 64 * WAVE;           // at most one 64-key step per lane
 constexpr int64_t IDX_MIN_WAVES = 32768;         // 32 wavefronts per SIMD
 
-__device__ __forceinline__ v4f mfma_fp8_16x16x128(const v8i &a, const v8i &b, const v4f &c) {
-  // Format 0 = FP8 E4M3 for both operands; E8M0 scale 127 = 2^0 (no scaling).
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0x7F7F7F7F, 0, 0x7F7F7F7F);
-}
-
-__device__ __forceinline__ v8i load32(const uint8_t *p) {
-  const uint4 x0 = *reinterpret_cast<const uint4 *>(p);
-  const uint4 x1 = *reinterpret_cast<const uint4 *>(p + 16);
-  v8i r;
-  r[0] = (int)x0.x; r[1] = (int)x0.y; r[2] = (int)x0.z; r[3] = (int)x0.w;
-  r[4] = (int)x1.x; r[5] = (int)x1.y; r[6] = (int)x1.z; r[7] = (int)x1.w;
-  return r;
-}
-
 struct KeyStep {
   v8i b[4];
   float ks;

@@ -1,0 +1,331 @@
+// Backward of the lightning-indexer score into its inputs.
+//
+// Page "arXiv'25 | DSA ... DeepSeek-V3.2", section 3 (first equation: the
+// score I[t,s] = sum_j w[t,j] ReLU(q[t,j] . k[s])) and section 5 (only the
+// indexer learns from its alignment loss; its inputs are detached from the
+// main model).  Given g[t,s] = dL/dI[t,s] over each query's set, the gradients
+// with respect to the head weights and the dequantised FP8 query and key
+// (qh = q_scale * q8, kh = k_scale * k8; the quantiser passes gradients
+// unchanged; the derivative of ReLU at 0 is taken as 0):
+//   dw[t,j]     = q_scale[t,j] * sum_s c_s * max(D_js, 0)
+//   dqh[t,j,:]  = w[t,j] * sum_s [D_js > 0] c_s k8_s
+//   dkh[r(s),:] += g_s * sum_j [D_js > 0] e_j q8_j
+// with D_js = q8_j . k8_s (exact FP8 products, summed in fp32),
+// c_s = g_s * k_scale_s and e_j = w[t,j] * q_scale[t,j].
+//
+// One block (4 wavefronts) = one query and a run of up to 2048 members of its
+// set, in tiles of 64 keys:
+//   * D on FP8 MFMA (v_mfma_scale_f32_16x16x128_f8f6f4), as in the forward
+//     indexer: wavefront w scores keys 16w .. 16w+15 of the tile against all 64
+//     heads, the keys loaded straight into B-operand registers (the next tile's
+//     one tile ahead);
+//   * the 0/1 gates [D > 0] go to LDS as a [key][head] and a [head][key] bf16
+//     matrix, and c_s k8_s as a [dim][key] pair of bf16 matrices hi + lo
+//     (hi = bf16(x), lo = bf16(x - hi); hi + lo is within 2^-17 |x| of x), so that
+//     both contractions run on bf16 MFMA (v_mfma_f32_32x32x16_bf16) with
+//     products exact in fp32;
+//   * dkh of the tile = gates[key][head] . (e q8)[head][dim], whose B operand
+//     (hi + lo) stays in registers for the whole block, then times g_s into dk
+//     by fp32 atomic adds (a key row may belong to several queries);
+//   * dqh += gates[head][key] . (c k8)[key][dim] accumulates in registers over
+//     the block's tiles; dw accumulates in-lane from D.
+// Wavefront w owns the 32 x 64 quarter (rows 32 (w & 1), columns 64 (w >> 1))
+// of both 64 x 128 products.  Rows of the LDS matrices are padded to 144
+// bytes, so the 16-byte fragment reads of 32 consecutive rows spread over the
+// banks.
+#include "device_util.h"
+#include "dsa_internal.h"
+
+namespace dsa {
+
+constexpr int IB_THREADS = 256;
+constexpr int IB_TILE = 64;                 // keys per tile
+constexpr int IB_MAX_MEMBERS = 2048;        // members per block
+constexpr int IB_PER_THREAD = IB_MAX_MEMBERS / IB_THREADS;
+constexpr int IB_MIN_BLOCKS = 1024;
+constexpr int IB_LD = 72;                   // bf16 per padded LDS row (144 bytes)
+constexpr uint32_t IB_INVALID = 0x80000000u;
+constexpr uint16_t BF16_ONE = 0x3F80;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+
+struct IndexerBwdArgs {
+  IndexerBwdLaunch a;
+  int nchunk;
+  int members;  // per block, a multiple of IB_TILE
+};
+
+__device__ __forceinline__ uint16_t bf16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, (__bf16)x);  // round to nearest even
+}
+__device__ __forceinline__ float bf16_value(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+__device__ __forceinline__ bf16x8_t as_bf8(const uint4 &u) { return __builtin_bit_cast(bf16x8_t, u); }
+// The four FP8 E4M3 bytes of word v as fp32 (exact), lowest byte first.
+__device__ __forceinline__ void fp8x4(uint32_t v, float *f) {
+  f[0] = __builtin_amdgcn_cvt_f32_fp8((int)v, 0);
+  f[1] = __builtin_amdgcn_cvt_f32_fp8((int)v, 1);
+  f[2] = __builtin_amdgcn_cvt_f32_fp8((int)v, 2);
+  f[3] = __builtin_amdgcn_cvt_f32_fp8((int)v, 3);
+}
+
+__global__ __launch_bounds__(256) void ib_zero_kernel(float *__restrict__ p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0.0f;
+}
+
+__global__ __launch_bounds__(IB_THREADS) void indexer_bwd_kernel(IndexerBwdArgs p) {
+  const IndexerBwdLaunch &a = p.a;
+  const int t = blockIdx.x / p.nchunk;
+  const int chunk = blockIdx.x - t * p.nchunk;
+  const int nvis = a.q_nvis[t];
+  int nset = nvis;
+  if (a.idx) {
+    const int c = a.count ? a.count[t] : a.k;
+    nset = max(0, min(c, min(a.k, nvis)));
+  }
+  const int m0 = chunk * p.members;
+  const int nmem = min(p.members, nset - m0);
+  if (nmem <= 0) return;  // block-uniform
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int l15 = lane & 15, g4 = lane >> 4;    // FP8 MFMA lane split
+  const int l31 = lane & 31, g2 = lane >> 5;    // bf16 32x32 MFMA lane split
+  const int half = wave & 1, dn0 = 2 * (wave >> 1);
+
+  __shared__ __attribute__((aligned(16))) uint16_t gk[IB_TILE * IB_LD];    // [key][head] gates
+  __shared__ __attribute__((aligned(16))) uint16_t gh[64 * IB_LD];         // [head][key] gates
+  __shared__ __attribute__((aligned(16))) uint16_t chi[128 * IB_LD];       // [dim][key] c k8, hi
+  __shared__ __attribute__((aligned(16))) uint16_t clo[128 * IB_LD];       // [dim][key] c k8, lo
+  __shared__ uint32_t mrow[IB_MAX_MEMBERS];  // physical row (IB_INVALID: not a member)
+  __shared__ float mg[IB_MAX_MEMBERS];       // g_s (0 for non-members)
+  __shared__ float mc[IB_MAX_MEMBERS];       // c_s = g_s * k_scale_s
+  __shared__ float dwred[4][64];
+
+  // Members -> rows, g and c, all loads issued before any is used.  A
+  // non-member (outside [0, n_vis), or past the run) reads position 0's row
+  // with g = 0, so it adds nothing, and its dk atomics are skipped.
+  const int seq = a.q_seq[t];
+  const int ntile = (nmem + IB_TILE - 1) / IB_TILE;
+  {
+    int pos[IB_PER_THREAD];
+    float gv[IB_PER_THREAD];
+    const int lastm = nmem - 1;
+#pragma unroll
+    for (int j = 0; j < IB_PER_THREAD; ++j) {
+      const int i = min(tid + j * IB_THREADS, lastm);
+      pos[j] = a.idx ? a.idx[(int64_t)t * a.k + m0 + i] : m0 + i;
+    }
+#pragma unroll
+    for (int j = 0; j < IB_PER_THREAD; ++j) {
+      const int i = min(tid + j * IB_THREADS, lastm);
+      const bool ok = pos[j] >= 0 && pos[j] < nvis;
+      gv[j] = a.grad[(int64_t)t * a.ld_grad + (a.idx ? m0 + i : (ok ? pos[j] : 0))];
+      pos[j] = ok ? pos[j] : -1;
+    }
+    uint32_t row[IB_PER_THREAD];
+#pragma unroll
+    for (int j = 0; j < IB_PER_THREAD; ++j) row[j] = (uint32_t)phys_row(a.map, seq, max(pos[j], 0));
+    float ks[IB_PER_THREAD];
+#pragma unroll
+    for (int j = 0; j < IB_PER_THREAD; ++j) ks[j] = a.k_scale[row[j]];
+#pragma unroll
+    for (int j = 0; j < IB_PER_THREAD; ++j) {
+      const int i = tid + j * IB_THREADS;
+      if (i < ntile * IB_TILE) {
+        const bool ok = i < nmem && pos[j] >= 0;
+        mrow[i] = row[j] | (ok ? 0u : IB_INVALID);
+        mg[i] = ok ? gv[j] : 0.0f;
+        mc[i] = ok ? gv[j] * ks[j] : 0.0f;
+      }
+    }
+  }
+
+  // Query-side operands.  A of the FP8 product: heads 16 mt + l15, bytes
+  // [32 g4, +32).  e_j = w_j q_scale_j.
+  const uint8_t *qp = a.q8 + (int64_t)t * (64 * 128);
+  v8i qa[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) qa[mt] = load32(qp + (16 * mt + l15) * 128 + 32 * g4);
+  // B of the dk product, [head][dim] = e_j q8[j][dim] as hi + lo: lane holds
+  // dim 32 (dn0 + nt) + l31, heads 16 ks + 8 g2 .. + 7.
+  uint4 bkh[2][4], bkl[2][4];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int d = 32 * (dn0 + nt) + l31;
+      uint16_t hi[8], lo[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int j = 16 * ks + 8 * g2 + e;
+        const float qs = a.q_scale ? a.q_scale[(int64_t)t * 64 + j] : 1.0f;
+        const float x = a.w[(int64_t)t * 64 + j] * qs * __builtin_amdgcn_cvt_f32_fp8((int)qp[j * 128 + d], 0);
+        hi[e] = bf16_bits(x);
+        lo[e] = bf16_bits(x - bf16_value(hi[e]));
+      }
+      bkh[nt][ks] = make_uint4(hi[0] | (uint32_t)hi[1] << 16, hi[2] | (uint32_t)hi[3] << 16,
+                               hi[4] | (uint32_t)hi[5] << 16, hi[6] | (uint32_t)hi[7] << 16);
+      bkl[nt][ks] = make_uint4(lo[0] | (uint32_t)lo[1] << 16, lo[2] | (uint32_t)lo[3] << 16,
+                               lo[4] | (uint32_t)lo[5] << 16, lo[6] | (uint32_t)lo[7] << 16);
+    }
+  __syncthreads();  // member table ready
+
+  v16f dq[2];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dq[nt][r] = 0.0f;
+  float dwa[4][4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dwa[mt][i] = 0.0f;
+
+  // Keys of tile tt for this wavefront: member 64 tt + 16 wave + l15, bytes
+  // [32 g4, +32) of its row (non-members read a valid row, see above).
+  auto load_keys = [&](int tt) {
+    const int mi = min(IB_TILE * tt + 16 * wave + l15, IB_TILE * ntile - 1);
+    const uint32_t r = mrow[mi] & ~IB_INVALID;
+    return load32(a.k8 + (int64_t)r * 128 + 32 * g4);
+  };
+
+  auto tile = [&](const int tt, const v8i &kb) {
+    const int mk = IB_TILE * tt + 16 * wave + l15;  // this lane's key (member index)
+    const float ck = mc[mk];
+    v4f d[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) d[mt] = mfma_fp8_16x16x128(qa[mt], kb, v4f{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dwa[mt][i] = fmaf(fmaxf(d[mt][i], 0.0f), ck, dwa[mt][i]);
+
+    __syncthreads();  // the previous tile's fragment reads are done
+    const int kl = 16 * wave + l15;  // key within the tile
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      uint16_t gt[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) gt[i] = d[mt][i] > 0.0f ? BF16_ONE : (uint16_t)0;
+      *reinterpret_cast<uint2 *>(&gk[kl * IB_LD + 16 * mt + 4 * g4]) =
+          make_uint2(gt[0] | (uint32_t)gt[1] << 16, gt[2] | (uint32_t)gt[3] << 16);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) gh[(16 * mt + 4 * g4 + i) * IB_LD + kl] = gt[i];
+    }
+    const uint32_t kw[8] = {(uint32_t)kb[0], (uint32_t)kb[1], (uint32_t)kb[2], (uint32_t)kb[3],
+                            (uint32_t)kb[4], (uint32_t)kb[5], (uint32_t)kb[6], (uint32_t)kb[7]};
+#pragma unroll
+    for (int wd = 0; wd < 8; ++wd) {
+      float kv[4];
+      fp8x4(kw[wd], kv);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const float x = ck * kv[b];
+        const uint16_t hi = bf16_bits(x);
+        const int o = (32 * g4 + 4 * wd + b) * IB_LD + kl;
+        chi[o] = hi;
+        clo[o] = bf16_bits(x - bf16_value(hi));
+      }
+    }
+    __syncthreads();  // gates and c k8 visible
+
+    // dkh of the tile's keys 32 half .. + 31, dims 32 (dn0 + nt) + l31.
+    v16f dk[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dk[nt][r] = 0.0f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const uint4 ga = *reinterpret_cast<const uint4 *>(&gk[(32 * half + l31) * IB_LD + 16 * ks + 8 * g2]);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        dk[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(ga), as_bf8(bkh[nt][ks]), dk[nt], 0, 0, 0);
+        dk[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(ga), as_bf8(bkl[nt][ks]), dk[nt], 0, 0, 0);
+      }
+    }
+    // dqh of heads 32 half .. + 31, dims 32 (dn0 + nt) + l31, over the tile's 64 keys.
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const uint4 ga = *reinterpret_cast<const uint4 *>(&gh[(32 * half + l31) * IB_LD + 16 * ks + 8 * g2]);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int o = (32 * (dn0 + nt) + l31) * IB_LD + 16 * ks + 8 * g2;
+        const uint4 bh = *reinterpret_cast<const uint4 *>(&chi[o]);
+        const uint4 bl = *reinterpret_cast<const uint4 *>(&clo[o]);
+        dq[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(ga), as_bf8(bh), dq[nt], 0, 0, 0);
+        dq[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(ga), as_bf8(bl), dq[nt], 0, 0, 0);
+      }
+    }
+    // dk rows: accumulator register r holds key 8 (r >> 2) + 4 g2 + (r & 3).
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int mi = IB_TILE * tt + 32 * half + 8 * (r >> 2) + 4 * g2 + (r & 3);
+      const uint32_t rw = mrow[mi];
+      const float gs = mg[mi];
+      if (!(rw & IB_INVALID)) {
+        float *dst = a.dk + (int64_t)rw * 128 + 32 * dn0 + l31;
+        unsafeAtomicAdd(dst, dk[0][r] * gs);
+        unsafeAtomicAdd(dst + 32, dk[1][r] * gs);
+      }
+    }
+  };
+
+  v8i kb0 = load_keys(0), kb1;
+  int tt = 0;
+  for (; tt + 1 < ntile; tt += 2) {
+    kb1 = load_keys(tt + 1);
+    tile(tt, kb0);
+    kb0 = load_keys(min(tt + 2, ntile - 1));
+    tile(tt + 1, kb1);
+  }
+  if (tt < ntile) tile(tt, kb0);
+
+  // dq: accumulator register r holds head 32 half + 8 (r >> 2) + 4 g2 + (r & 3).
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int h = 32 * half + 8 * (r >> 2) + 4 * g2 + (r & 3);
+      const float wv = a.w[(int64_t)t * 64 + h];
+      unsafeAtomicAdd(a.dq + ((int64_t)t * 64 + h) * 128 + 32 * (dn0 + nt) + l31, dq[nt][r] * wv);
+    }
+  // dw: sum over the 16 keys of the lane group, then over the wavefronts.
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v = dwa[mt][i];
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1) v += shfl_xor(v, m);
+      if (l15 == 0) dwred[wave][16 * mt + 4 * g4 + i] = v;
+    }
+  __syncthreads();
+  if (tid < 64) {
+    const float qs = a.q_scale ? a.q_scale[(int64_t)t * 64 + tid] : 1.0f;
+    const float v = (dwred[0][tid] + dwred[1][tid]) + (dwred[2][tid] + dwred[3][tid]);
+    unsafeAtomicAdd(a.dw + (int64_t)t * 64 + tid, v * qs);
+  }
+}
+
+hipError_t launch_indexer_bwd(const IndexerBwdLaunch &a, int max_set, hipStream_t st) {
+  if (a.num_q == 0) return hipSuccess;
+  const int64_t nz = (int64_t)a.num_q * 64 * 128;
+  hipLaunchKernelGGL(ib_zero_kernel, dim3((unsigned)((nz + 255) / 256)), dim3(256), 0, st, a.dq, nz);
+  hipLaunchKernelGGL(ib_zero_kernel, dim3((unsigned)(((int64_t)a.num_q * 64 + 255) / 256)), dim3(256), 0, st, a.dw,
+                     (int64_t)a.num_q * 64);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || max_set == 0) return e;
+  IndexerBwdArgs p;
+  p.a = a;
+  int members = IB_MAX_MEMBERS;
+  auto chunks = [&](int m) { return (max_set + m - 1) / m; };
+  while (members > IB_TILE && (int64_t)a.num_q * chunks(members) < IB_MIN_BLOCKS) members /= 2;
+  p.members = members;
+  p.nchunk = chunks(members);
+  hipLaunchKernelGGL(indexer_bwd_kernel, dim3((unsigned)((int64_t)a.num_q * p.nchunk)), dim3(IB_THREADS), 0, st, p);
+  return hipGetLastError();
+}
+
+}  // namespace dsa
