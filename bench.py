@@ -420,6 +420,13 @@ def kl_result(args):
     t_s = timed(lambda: dsa.dsa_indexer_kl_sparse(p["queries"], p["layout"], wl.q_mla, wl.kv, p["idx"], None, wl.k,
                                                   p["lse"], wl.softmax_scale, scores, grad_s, kl, loss=loss))
     loss_s = float(loss.item())
+    # Backward through the indexer score, from the sparse stage's dL/dI.
+    dq = torch.empty((nq, 64, 128), dtype=torch.float32, device="cuda")
+    dw = torch.empty((nq, 64), dtype=torch.float32, device="cuda")
+    dk = torch.zeros((wl.rows, 128), dtype=torch.float32, device="cuda")
+    log("kl: indexer backward, sparse stage")
+    tb_s = timed(lambda: dsa.dsa_indexer_backward(p["queries"], p["layout"], p["q8"], p["qs"], wl.w, p["k8"], p["ks"],
+                                                  p["idx"], None, wl.k, grad_s, dq, dw, dk))
     del grad_s
     log("kl: dense warm-up")
     lse_d = torch.empty((nq, 128), dtype=torch.float32, device="cuda")
@@ -429,7 +436,14 @@ def kl_result(args):
     t_d = timed(lambda: dsa.dsa_indexer_kl_dense(p["queries"], p["layout"], wl.q_mla, wl.kv, lse_d, wl.softmax_scale,
                                                  scores, grad_d, kl, loss=loss))
     loss_d = float(loss.item())
+    log("kl: indexer backward, dense warm-up")
+    tb_d = timed(lambda: dsa.dsa_indexer_backward(p["queries"], p["layout"], p["q8"], p["qs"], wl.w, p["k8"], p["ks"],
+                                                  None, None, 0, grad_d, dq, dw, dk))
+    del dq, dw, dk
     flop_member = 128 * 576 * 2
+    # Backward per (query, key) pair: the 64 x 128 FP8 dot products, then the
+    # dq and dk contractions (64 x 128 multiply-adds each).
+    bwd_flop = 3 * 64 * 128 * 2
     tf_s = members_s * flop_member / t_s / 1e12
     tf_d = members_d * flop_member / t_d / 1e12
     cpu = None
@@ -465,6 +479,10 @@ def kl_result(args):
         "sparse": {"members": members_s, "ms": 1e3 * t_s, "tflops_bf16": tf_s, "loss": loss_s},
         "dense_warmup": {"members": members_d, "ms": 1e3 * t_d, "tflops_bf16": tf_d,
                          "frac_bf16_peak": tf_d / BF16_PEAK_TFLOPS, "loss": loss_d},
+        "indexer_backward": {
+            "flop_per_pair": bwd_flop,
+            "sparse": {"pairs": members_s, "ms": 1e3 * tb_s, "tflops": members_s * bwd_flop / tb_s / 1e12},
+            "dense_warmup": {"pairs": members_d, "ms": 1e3 * tb_d, "tflops": members_d * bwd_flop / tb_d / 1e12}},
     })
     if cpu:
         result["cpu_baseline"] = cpu
