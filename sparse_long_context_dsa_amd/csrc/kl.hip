@@ -168,7 +168,7 @@ __global__ __launch_bounds__(MLA_THREADS, 2) void kl_target_kernel(KlTargetArgs 
     // K fragments are read four steps ahead of their MFMA.
     v16f s;
     {
-      constexpr int AHEAD = 4;
+      constexpr int AHEAD = 6;
       uint4 kf[AHEAD + 1];
 #pragma unroll
       for (int ks = 0; ks < AHEAD; ++ks)

@@ -13,8 +13,8 @@
 // for the whole run (36 x 16-byte B fragments, 144 VGPRs) and so does its
 // output accumulator O[32 heads, 512] in fp32 (16 x 32x32 tiles in AGPRs).
 // Rows arrive in tiles of 32, gathered through the position -> row map
-// straight from global memory into LDS (global_load_lds, 16 bytes per lane,
-// no staging registers), three tiles in flight.  One row-major copy of each
+// straight from global memory into LDS (buffer/global loads to LDS, 16 bytes
+// per lane, no staging registers), three tile buffers.  One row-major copy of each
 // tile serves both products:
 //   * S^T = K . Q^T (v_mfma_f32_32x32x16_bf16, M = rows, N = heads, K = 576
 //     in 36 steps): A fragments are 16-byte LDS reads of a row;
@@ -118,8 +118,6 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave-uniform
   const int g = lane >> 5, c = lane & 31;
-  const int dh = wave & 1;        // half of the value dims this wavefront accumulates
-  const int partner = wave ^ 1;   // the wavefront owning the other 32 heads of the pair
 
   // Three separately declared tile buffers: each has its own alias scope, so
   // the compiler sees that reading one tile never races with the LDS DMA that
@@ -130,15 +128,11 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
   // Physical row per selected position (bit 31: outside [0, n_vis)); the
   // tail keeps the masked reads of a partial last tile in bounds.
   __shared__ __attribute__((aligned(16))) uint32_t prow[MLA_MAX_ROWS + MLA_T];
-  // Per-tile exchange within a wavefront pair: P of the sender's 32 heads as
-  // bf16 A fragments (lane-major, 2 x 16 bytes per lane), the rescale flag
-  // and factors.  The in-order schedule uses slot 0 only: the partner's reads
-  // of tile t complete (their MFMAs consume them) before it reaches the
-  // barrier that precedes the sender's writes of tile t + 1.  The pipelined
-  // schedule consumes tile t's P one step later, so it alternates slots.
-  __shared__ __attribute__((aligned(16))) uint4 pex[2][MLA_WAVES][2][WAVE];
+  // Per-head rescale factors (two slots: the pipelined schedule reads tile
+  // t's at step t + 1) and 1/l for the epilogue, each wavefront's own: they
+  // carry a head's value from the lane that owns its softmax state to the
+  // lanes that hold its O rows.
   __shared__ __attribute__((aligned(16))) float aex[2][MLA_WAVES][32];
-  __shared__ int fex[2][MLA_WAVES];
   __shared__ __attribute__((aligned(16))) float iex[MLA_WAVES][32];  // 1/l per head, for the epilogue
 
   const int nvis = a.q_nvis[q];
@@ -219,15 +213,12 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
 
   const int head = 32 * wave + c;
 
-  // O[mt][nt]: M-tile 0 = own heads, 1 = partner heads; N-tile nt = value
-  // dims 256*dh + 32*nt .. +31.
-  v16f o[2][8];
+  // O[nt]: the 32 own heads x value dims 32*nt .. +31 (all 512 dims).
+  v16f o[16];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int nt = 0; nt < 16; ++nt)
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[mt][nt][i] = 0.0f;
+    for (int i = 0; i < 16; ++i) o[nt][i] = 0.0f;
   float m_ref = -INFINITY, l_run = 0.0f;  // per own head c (both lane halves agree on m_ref)
 
   // Per-lane LDS address bases (everything else is an immediate offset).
@@ -249,7 +240,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
   for (int odd = 0; odd < 2; ++odd)
 #pragma unroll
     for (int half = 0; half < 2; ++half)
-      tr_base[odd][half] = tile_off(8 * half + 4 * g + tr_r, 32 * dh + 4 * odd + tr_x) + 8 * tr_piece;
+      tr_base[odd][half] = tile_off(8 * half + 4 * g + tr_r, 4 * odd + tr_x) + 8 * tr_piece;
 
   // prow ready; does any row need masking beyond a partial last tile?
   const bool any_bad = __syncthreads_or(bad) != 0;
@@ -277,7 +268,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
   // are read QK_AHEAD steps ahead of their MFMA (ring buffer); hook(ks) runs
   // after the MFMA of step ks.
   auto qk = [&](const uint8_t *buf, v16f &s, auto &&hook) {
-    constexpr int QK_AHEAD = 4;
+    constexpr int QK_AHEAD = 6;
     uint4 kf[QK_AHEAD + 1];
 #pragma unroll
     for (int ks = 0; ks < QK_AHEAD; ++ks)
@@ -365,20 +356,20 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
     }
   };
 
-    // O += P . V over the tile's 32 rows (2 k-steps of 16), for both head
-    // sets of the pair; each V fragment feeds two MFMAs.  The k-slots of lane
-    // group g in step ks2 are rows 16*ks2 + 4g + {0..3} and 16*ks2 + 8 + 4g +
-    // {0..3} (where the S^T accumulator put them, in both wavefronts); the
-    // transposing read gives lane l the 4 rows of one of those sets at column
-    // n = l % 32: lanes 4r..4r+3 of each 16-lane group point at row r of the
-    // set, 4 columns each.  16 steps j = (ks2, nt); the B fragment of step j
-    // is read PV_AHEAD steps ahead of its MFMAs (ring buffer).  hook(j) runs
-    // between the two MFMAs of step j.
-  auto pv = [&](const uint8_t *buf, const uint4 &a0, const uint4 &a1, const uint4 &b0, const uint4 &b1,
-                auto &&hook) {
-    constexpr int PV_AHEAD = PIPE ? 2 : 4;
+  // O += P . V over the tile's 32 rows (2 k-steps of 16) for the 32 own
+  // heads and all 512 value dims (16 N-tiles).  The k-slots of lane group g
+  // in step ks2 are rows 16*ks2 + 4g + {0..3} and 16*ks2 + 8 + 4g + {0..3}
+  // (where the S^T accumulator put them); the transposing read gives lane l
+  // the 4 rows of one of those sets at column n = l % 32: lanes 4r..4r+3 of
+  // each 16-lane group point at row r of the set, 4 columns each.  32 steps
+  // j = (ks2, nt); the B fragment of step j is read PV_AHEAD steps ahead of
+  // its MFMA (ring buffer).  hook(j) runs after the MFMA of step j.  Each
+  // wavefront reads the whole value half of the tile, so no P leaves the
+  // wavefront and no barrier separates the softmax from the PV.
+  auto pv = [&](const uint8_t *buf, const uint4 &a0, const uint4 &a1, auto &&hook) {
+    constexpr int PV_AHEAD = PIPE ? 3 : 4;
     auto v_frag = [&](int j) {
-      const int ks2 = j >> 3, nt = j & 7;
+      const int ks2 = j >> 4, nt = j & 15;
       const int off0 = tr_base[nt & 1][0] + 9216 * (2 * ks2) + 1024 * (nt >> 1);  // half 0
       const int off1 = tr_base[nt & 1][1] + 9216 * (2 * ks2) + 1024 * (nt >> 1);  // half 1
       const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)(buf + off0));
@@ -390,28 +381,28 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
 #pragma unroll
     for (int j = 0; j < PV_AHEAD; ++j) vf[j] = v_frag(j);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      if (j + PV_AHEAD < 16) vf[(j + PV_AHEAD) % (PV_AHEAD + 1)] = v_frag(j + PV_AHEAD);
-      const int nt = j & 7;
-      const v8bf vb = as_bf(vf[j % (PV_AHEAD + 1)]);
-      o[0][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(j < 8 ? a0 : a1), vb, o[0][nt], 0, 0, 0);
+    for (int j = 0; j < 32; ++j) {
+      if (j + PV_AHEAD < 32) vf[(j + PV_AHEAD) % (PV_AHEAD + 1)] = v_frag(j + PV_AHEAD);
+      const int nt = j & 15;
+      o[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(j < 16 ? a0 : a1), as_bf(vf[j % (PV_AHEAD + 1)]), o[nt], 0,
+                                                     0, 0);
       hook(j);
-      o[1][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf(j < 8 ? b0 : b1), vb, o[1][nt], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
 
-  // O rows of own heads (mt 0) or of the partner's (mt 1) times per-head factors.
-  auto rescale_o = [&](const int mt, const float *fac) {
+  // O rows (own heads 8i + 4g + j) times their heads' factors, from this
+  // wavefront's 32-entry slot in LDS.
+  auto rescale_o = [&](const float *fac) __attribute__((always_inline)) {
     float al[16];
     read_head_values(fac, g, al);
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt)
+    for (int nt = 0; nt < 16; ++nt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        float x = o[mt][nt][i];
+        float x = o[nt][i];
         scale_acc(x, al[i]);
-        o[mt][nt][i] = x;
+        o[nt][i] = x;
       }
   };
 
@@ -429,17 +420,10 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
-  // LDS writes done, then a bare barrier (the DMA of later tiles stays in flight).
-  auto publish = [&]() {
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-  };
   if (!PIPE) {
     // In-order schedule (decode, where the gathers come from HBM): the
     // gather of tile t + 2 starts as tile t's compute starts, two tiles
-    // ahead; then QK, softmax, exchange and PV of tile t.
+    // ahead; then QK, softmax and PV of tile t.
     auto tile_step = [&](const int t, const uint8_t *buf, uint8_t *nbuf) {
       wait_tile(t);
       // The buffer of tile t-1 is free now (every wave is past its compute):
@@ -459,20 +443,13 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
       uint32_t pk[8];
 #pragma unroll
       for (int j = 0; j < 10; ++j) softmax_piece(j, z, zscale, tmax, resc, alpha, nmref, psum, pk);
-      if (resc && g == 0) aex[0][wave][c] = alpha;
-      if (lane == 0) fex[0][wave] = resc ? 1 : 0;
       const uint4 pa0 = make_uint4(pk[0], pk[1], pk[2], pk[3]);
       const uint4 pa1 = make_uint4(pk[4], pk[5], pk[6], pk[7]);
-      pex[0][wave][0][lane] = pa0;
-      pex[0][wave][1][lane] = pa1;
-      publish();
-      const uint4 pp0 = pex[0][partner][0][lane];
-      const uint4 pp1 = pex[0][partner][1][lane];
-      if (t > 0) {  // O is still zero on the first tile
-        if (resc) rescale_o(0, aex[0][wave]);
-        if (fex[0][partner]) rescale_o(1, aex[0][partner]);
+      if (t > 0 && resc) {  // O is still zero on the first tile
+        if (g == 0) aex[0][wave][c] = alpha;  // own slot: no other wavefront reads it
+        rescale_o(aex[0][wave]);
       }
-      pv(buf, pa0, pa1, pp0, pp1, no_hook);
+      pv(buf, pa0, pa1, no_hook);
     };
     for (int t = 0; t < ntiles; t += NBUF) {
       tile_step(t, tb0, tb2);
@@ -484,13 +461,14 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
     // tile t's QK, with the gather of tile t + 1 issued between its MFMAs;
     // then tile t-1's PV with tile t's softmax spread between its MFMAs, so
     // the matrix cores, the vector ALUs and the memory pipeline work at once.
-    // P of tile t is consumed one tile later, so the exchange slots
-    // alternate, and O is rescaled for tile t's reference max just before
-    // that PV (the partner's flag is read a whole QK earlier).
+    // P of tile t stays in registers for one tile, and O is rescaled for
+    // tile t's reference max just before that PV (the factors' LDS slots
+    // alternate).
     bool resc_prev = false;
-    int pflag_prev = 0;
-    // Tile t-1's buffer is free once the publishing barrier of tile t-1 has
-    // been passed; tile t + 1 goes into the buffer of tile t - 2.
+    uint4 pp0 = make_uint4(0u, 0u, 0u, 0u), pp1 = pp0;  // P of the previous tile, kept in registers
+    // Tile t-1's buffer is free once every wavefront has passed the barrier of
+    // tile t (its PV of tile t-2 is done); tile t + 1 goes into the buffer of
+    // tile t - 2.
     auto tile_step = [&](const int t, const uint8_t *buf, uint8_t *nbuf, const uint8_t *pbuf, auto prev) {
       constexpr bool PREV = decltype(prev)::value;
       wait_tile(t);
@@ -506,27 +484,19 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
       float alpha, nmref, psum;
       uint32_t pk[8];
       if (PREV) {
-        const int ps = (t - 1) & 1;
-        if (resc_prev) rescale_o(0, aex[ps][wave]);
-        if (pflag_prev) rescale_o(1, aex[ps][partner]);
-        const uint4 qa0 = pex[ps][wave][0][lane], qa1 = pex[ps][wave][1][lane];
-        const uint4 qp0 = pex[ps][partner][0][lane], qp1 = pex[ps][partner][1][lane];
-        pv(pbuf, qa0, qa1, qp0, qp1, [&](const int j) {
+        if (resc_prev) rescale_o(aex[(t - 1) & 1][wave]);
+        pv(pbuf, pp0, pp1, [&](const int j) {
           if (j < 10) softmax_piece(j, z, zscale, tmax, resc, alpha, nmref, psum, pk);
         });
       } else {
 #pragma unroll
         for (int j = 0; j < 10; ++j) softmax_piece(j, z, zscale, tmax, resc, alpha, nmref, psum, pk);
       }
-      const int sl = t & 1;
-      if (g == 0) aex[sl][wave][c] = alpha;
-      if (lane == 0) fex[sl][wave] = resc ? 1 : 0;
-      pex[sl][wave][0][lane] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-      pex[sl][wave][1][lane] = make_uint4(pk[4], pk[5], pk[6], pk[7]);
-      publish();
+      if (g == 0) aex[t & 1][wave][c] = alpha;  // own slot, read at the next step
+      pp0 = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+      pp1 = make_uint4(pk[4], pk[5], pk[6], pk[7]);
       // O is still zero until tile 0's PV, which tile 0's factors precede.
       resc_prev = PREV && resc;
-      pflag_prev = PREV ? fex[sl][partner] : 0;
     };
     using First = std::integral_constant<bool, false>;
     using Later = std::integral_constant<bool, true>;
@@ -537,20 +507,17 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
       if (t + 2 < ntiles) tile_step(t + 2, tb0, tb1, tb2, Later{});
     }
     if (ntiles > 0) {
-      const int lt = (ntiles - 1) % NBUF, ps = (ntiles - 1) & 1;
-      if (resc_prev) rescale_o(0, aex[ps][wave]);
-      if (pflag_prev) rescale_o(1, aex[ps][partner]);
-      const uint4 qa0 = pex[ps][wave][0][lane], qa1 = pex[ps][wave][1][lane];
-      const uint4 qp0 = pex[ps][partner][0][lane], qp1 = pex[ps][partner][1][lane];
-      pv(lt == 0 ? tb0 : lt == 1 ? tb1 : tb2, qa0, qa1, qp0, qp1, no_hook);
+      const int lt = (ntiles - 1) % NBUF;
+      if (resc_prev) rescale_o(aex[(ntiles - 1) & 1][wave]);
+      pv(lt == 0 ? tb0 : lt == 1 ? tb1 : tb2, pp0, pp1, no_hook);
     }
   }
   // The last two tiles issued gathers past the end: let them land before the
   // block's LDS can be handed to another block.
   __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0)
 
-  // Normalise.  Both lane halves hold partial sums of own head c; the pair
-  // exchanges 1/l so that each wavefront can scale its partner's head rows.
+  // Normalise.  Both lane halves hold partial sums of own head c; 1/l goes
+  // through the wavefront's LDS slot to the lanes that hold that head's rows.
   const float l_tot = xhalf_sum(l_run);
   const float inv = (l_tot > 0.0f) ? 1.0f / l_tot : 0.0f;
   const float lse_v = (l_tot > 0.0f) ? m_ref * LN2 + logf(l_tot) : -INFINITY;
@@ -567,19 +534,17 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
     lbase = p.part_lse + ((int64_t)q * p.nsplit + sp) * 128;
   }
   // Each value is scaled by its head's 1/l on its way out of the AGPRs.
-#pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
-    const int hset = 32 * (mt == 0 ? wave : partner);
+  {
     float il[16];
-    read_head_values(iex[mt == 0 ? wave : partner], g, il);
+    read_head_values(iex[wave], g, il);
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt)
+    for (int nt = 0; nt < 16; ++nt)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int h = hset + 8 * i + 4 * g + j;
-          obase[(int64_t)h * 512 + 256 * dh + 32 * nt + c] = read_scaled(o[mt][nt][4 * i + j], il[4 * i + j]);
+          const int h = 32 * wave + 8 * i + 4 * g + j;
+          obase[(int64_t)h * 512 + 32 * nt + c] = read_scaled(o[nt][4 * i + j], il[4 * i + j]);
         }
   }
   if (lbase && g == 0) lbase[head] = lse_v;
