@@ -111,3 +111,55 @@ def test_empty_batches_are_accepted_without_launching():
     assert L.dsa_indexer_scores(ctypes.byref(q), ctypes.byref(lay), None, None, None, None, None, None, 0,
                                 None) == 0
     assert L.dsa_quantize_fp8(None, 0, 128, None, None, None) == 0
+
+
+def test_kl_and_backward_argument_checks():
+    """The indexer-loss and indexer-backward calls validate on the host."""
+    L = _lib.lib()
+    q = _queries(3, 5000)
+    p = ctypes.c_void_p(0x1000)
+    odd = ctypes.c_void_p(0x1002)
+    lay = _lib.KvLayoutC(1, 0, 0, 0, 5000, None, p.value)
+    # sparse KL: idx required, k in [1, 2048], ld_scores >= max_nvis, 16-byte aligned q / kv
+    st = L.dsa_indexer_kl_sparse(ctypes.byref(q), ctypes.byref(lay), p, p, None, None, 2048, p, 0.07, p, 5000, p,
+                                 None, p, None, None)
+    assert st == _lib.DSA_ERR_INVALID_ARG and b"idx" in L.dsa_last_error()
+    st = L.dsa_indexer_kl_sparse(ctypes.byref(q), ctypes.byref(lay), p, p, p, None, 4096, p, 0.07, p, 5000, p,
+                                 None, p, None, None)
+    assert st == _lib.DSA_ERR_INVALID_ARG and b"k =" in L.dsa_last_error()
+    st = L.dsa_indexer_kl_sparse(ctypes.byref(q), ctypes.byref(lay), p, p, p, None, 2048, p, 0.07, p, 4999, p,
+                                 None, p, None, None)
+    assert st == _lib.DSA_ERR_INVALID_ARG and b"ld_scores" in L.dsa_last_error()
+    st = L.dsa_indexer_kl_sparse(ctypes.byref(q), ctypes.byref(lay), odd, p, p, None, 2048, p, 0.07, p, 5000, p,
+                                 None, p, None, None)
+    assert st == _lib.DSA_ERR_INVALID_ARG
+    st = L.dsa_indexer_kl_sparse(ctypes.byref(q), ctypes.byref(lay), p, p, p, None, 2048, None, 0.07, p, 5000,
+                                 p, None, p, None, None)
+    assert st == _lib.DSA_ERR_INVALID_ARG  # lse missing
+    # dense KL: ld_grad >= max_nvis
+    st = L.dsa_indexer_kl_dense(ctypes.byref(q), ctypes.byref(lay), p, p, p, 0.07, p, 5000, p, None, 4000, p,
+                                None, None)
+    assert st == _lib.DSA_ERR_INVALID_ARG and b"ld_grad" in L.dsa_last_error()
+    # backward: non-null outputs, k checked when idx is given, ld_grad when it is not
+    st = L.dsa_indexer_backward(ctypes.byref(q), ctypes.byref(lay), p, None, p, p, p, p, None, 0, p, 0, p, p, p,
+                                None)
+    assert st == _lib.DSA_ERR_INVALID_ARG and b"k =" in L.dsa_last_error()
+    st = L.dsa_indexer_backward(ctypes.byref(q), ctypes.byref(lay), p, None, p, p, p, None, None, 0, p, 100, p, p,
+                                p, None)
+    assert st == _lib.DSA_ERR_INVALID_ARG and b"ld_grad" in L.dsa_last_error()
+    st = L.dsa_indexer_backward(ctypes.byref(q), ctypes.byref(lay), p, None, p, p, p, p, None, 2048, p, 2048, p,
+                                p, None, None)
+    assert st == _lib.DSA_ERR_INVALID_ARG  # dk missing
+    st = L.dsa_indexer_backward(ctypes.byref(q), ctypes.byref(lay), odd, None, p, p, p, p, None, 2048, p, 2048, p,
+                                p, p, None)
+    assert st == _lib.DSA_ERR_INVALID_ARG  # misaligned q_fp8
+
+
+def test_kl_and_backward_accept_empty_batches():
+    L = _lib.lib()
+    q = _lib.QueriesC(0, 0, None, None)
+    lay = _lib.KvLayoutC(0, 0, 0, 0, 0, None, None)
+    assert L.dsa_indexer_backward(ctypes.byref(q), ctypes.byref(lay), None, None, None, None, None, None, None, 0,
+                                  None, 0, None, None, None, None) == 0
+    assert L.dsa_indexer_kl_dense(ctypes.byref(q), ctypes.byref(lay), None, None, None, 0.07, None, 0, None, None, 0,
+                                  None, None, None) == 0

@@ -199,3 +199,27 @@ def test_backward_dk_accumulates_and_dq_is_deterministic():
     # the largest entry (the rounding of such sums), not relative per entry.
     one, two = outs[0][2].astype(np.float64), outs[1][2].astype(np.float64)
     assert np.abs(two - 2 * one).max() <= 1e-5 * np.abs(one).max()
+
+
+def test_backward_zero_upstream_and_count_null():
+    """grad = 0 gives dq = dw = 0 exactly and leaves dk unchanged; count = NULL
+    means min(k, n_vis) members."""
+    banner("indexer backward zero grad / count NULL")
+    wl = make_custom(seq_lens=[300, 2500], device="cuda", seed=76)
+    g = GpuInputs(wl)
+    k = 512
+    idx, cnt = random_selection(wl, k, 10)
+    gi = torch.from_numpy(idx).cuda()
+    dq = torch.full((wl.nq, 64, 128), float("nan"), dtype=torch.float32, device="cuda")
+    dw = torch.full((wl.nq, 64), float("nan"), dtype=torch.float32, device="cuda")
+    dk = torch.full((wl.rows, 128), 0.25, dtype=torch.float32, device="cuda")
+    zero = torch.zeros((wl.nq, k), dtype=torch.float32, device="cuda")
+    dsa.dsa_indexer_backward(g.queries, g.layout, g.q8, g.qs, wl.w, g.k8, g.ks, gi, None, k, zero, dq, dw, dk)
+    torch.cuda.synchronize()
+    assert (dq == 0).all() and (dw == 0).all() and (dk == 0.25).all()
+    # count NULL against the explicit count
+    grad_h = (np.random.default_rng(11).standard_normal((wl.nq, k)) * 1e-2).astype(np.float32)
+    a = run_bwd(g, idx, None, k, grad_h)
+    b = run_bwd(g, idx, cnt, k, grad_h)
+    for x, y in zip(a, b):
+        assert np.allclose(x, y, rtol=1e-6, atol=1e-7 * max(1.0, np.abs(y).max()))

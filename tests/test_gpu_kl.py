@@ -227,3 +227,22 @@ def test_deterministic():
     b = run_sparse(wl, idx, cnt, k, s_d, lse=a[4])
     for x, y in zip(a[:3], b[:3]):
         assert (x.view(np.uint32) == y.view(np.uint32)).all()
+
+
+def test_kl_degenerate_cases():
+    """k = 1 (every set one member: p = Softmax = 1, KL = 0, gradient 0), and an
+    empty batch, which still writes the loss (0)."""
+    banner("kl degenerate")
+    wl = make_custom(seq_lens=[5, 3000], device="cuda", seed=68)
+    idx, cnt = random_selection(wl, 1, 16)
+    _, s_d = synthetic_scores(wl, 17)
+    grad, target, kl, loss, _ = run_sparse(wl, idx, cnt, 1, s_d)
+    assert (kl == 0).all() and (grad == 0).all() and (target == 1).all() and loss == 0.0
+    q = dsa.Queries(wl.q_seq[:0], wl.q_nvis[:0], 0)
+    _, lay = layout_of(wl)
+    loss_t = torch.full((1,), float("nan"), dtype=torch.float32, device="cuda")
+    e = torch.empty((0,), dtype=torch.float32, device="cuda")
+    dsa.dsa_indexer_kl_dense(q, lay, wl.q_mla[:0], wl.kv, e.view(0, 128), wl.softmax_scale, e.view(0, 64),
+                             e.view(0, 64), e, loss=loss_t)
+    torch.cuda.synchronize()
+    assert loss_t.item() == 0.0
