@@ -312,7 +312,7 @@ int dsa_indexer_backward(const dsa_queries *qr, const dsa_kv_layout *ly, const u
   }
   const int max_set = sparse ? (qr->max_nvis < k ? qr->max_nvis : k) : qr->max_nvis;
   dsa::IndexerBwdLaunch a{q_fp8, q_scale, w, k_fp8, k_scale, idx, count, qr->q_seq, qr->q_nvis, m,
-                          sparse ? k : 0, qr->num_q, grad, ld_grad, dq, dw, dk};
+                          sparse ? k : 0, qr->num_q, grad, ld_grad, dq, dw, dk, ly->num_seqs};
   return hip_status(dsa::launch_indexer_bwd(a, max_set, stream), "indexer backward launch");
 }
 

@@ -147,6 +147,7 @@ struct IndexerBwdLaunch {
   float *dq;             // [num_q, 64, 128]
   float *dw;             // [num_q, 64]
   float *dk;             // [rows, 128], added to
+  int32_t num_seqs;      // sequences of the layout (the dense mode's key tiles)
 };
 hipError_t launch_indexer_bwd(const IndexerBwdLaunch &a, int max_set, hipStream_t st);
 

@@ -73,6 +73,7 @@ __global__ __launch_bounds__(256) void ib_zero_kernel(float *__restrict__ p, int
   if (i < n) p[i] = 0.0f;
 }
 
+template <bool DK>
 __global__ __launch_bounds__(IB_THREADS) void indexer_bwd_kernel(IndexerBwdArgs p) {
   const IndexerBwdLaunch &a = p.a;
   const int t = blockIdx.x / p.nchunk;
@@ -154,6 +155,7 @@ __global__ __launch_bounds__(IB_THREADS) void indexer_bwd_kernel(IndexerBwdArgs 
   for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
+      if (!DK) break;
       const int d = 32 * (dn0 + nt) + l31;
       uint16_t hi[8], lo[8];
 #pragma unroll
@@ -208,8 +210,9 @@ __global__ __launch_bounds__(IB_THREADS) void indexer_bwd_kernel(IndexerBwdArgs 
       uint16_t gt[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) gt[i] = d[mt][i] > 0.0f ? BF16_ONE : (uint16_t)0;
-      *reinterpret_cast<uint2 *>(&gk[kl * IB_LD + 16 * mt + 4 * g4]) =
-          make_uint2(gt[0] | (uint32_t)gt[1] << 16, gt[2] | (uint32_t)gt[3] << 16);
+      if (DK)
+        *reinterpret_cast<uint2 *>(&gk[kl * IB_LD + 16 * mt + 4 * g4]) =
+            make_uint2(gt[0] | (uint32_t)gt[1] << 16, gt[2] | (uint32_t)gt[3] << 16);
 #pragma unroll
       for (int i = 0; i < 4; ++i) gh[(16 * mt + 4 * g4 + i) * IB_LD + kl] = gt[i];
     }
@@ -238,6 +241,7 @@ __global__ __launch_bounds__(IB_THREADS) void indexer_bwd_kernel(IndexerBwdArgs 
       for (int r = 0; r < 16; ++r) dk[nt][r] = 0.0f;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
+      if (!DK) break;
       const uint4 ga = *reinterpret_cast<const uint4 *>(&gk[(32 * half + l31) * IB_LD + 16 * ks + 8 * g2]);
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
@@ -261,6 +265,7 @@ __global__ __launch_bounds__(IB_THREADS) void indexer_bwd_kernel(IndexerBwdArgs 
     // dk rows: accumulator register r holds key 8 (r >> 2) + 4 g2 + (r & 3).
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
+      if (!DK) break;
       const int mi = IB_TILE * tt + 32 * half + 8 * (r >> 2) + 4 * g2 + (r & 3);
       const uint32_t rw = mrow[mi];
       const float gs = mg[mi];
@@ -309,6 +314,176 @@ __global__ __launch_bounds__(IB_THREADS) void indexer_bwd_kernel(IndexerBwdArgs 
   }
 }
 
+// dkh for the dense mode (every visible position), key-major: one block = one
+// 64-key tile of one sequence and a run of IBK_QRUN query indices; it loops
+// over the queries of that run that see any key of the tile and accumulates
+// dkh[key] = sum_t g_ts sum_j [D_tjs > 0] e_tj q8_tj in registers, then adds
+// its sum into dk (a handful of atomic adds per block instead of 128 per
+// (query, key) pair).  Per query:
+//   * D^T = K . Q^T on FP8 MFMA: the tile's keys are the A operand for the
+//     whole block (all 64 keys in every wavefront), wavefront w takes heads
+//     16w .. 16w+15 of the query as the B operand;
+//   * a[key][head] = [D > 0] e_j g_s goes to LDS as bf16 hi + lo and q8 as a
+//     [dim][head] bf16 matrix, and dkh += a . q8 runs on bf16 MFMA with the
+//     same 32 x 64 quarters per wavefront as the query-major kernel.
+// Query order within a block is the index order (a block-wide scan), so a
+// block's sum is deterministic; blocks of the same tile meet in the atomic adds.
+constexpr int IBK_QRUN = 512;  // query indices per block
+
+struct IndexerBwdDkArgs {
+  IndexerBwdLaunch a;
+  int tiles;   // key tiles per sequence
+  int qruns;   // query runs
+};
+
+__global__ __launch_bounds__(IB_THREADS) void indexer_bwd_dk_kernel(IndexerBwdDkArgs p) {
+  const IndexerBwdLaunch &a = p.a;
+  const int per_seq = p.tiles * p.qruns;
+  const int seq = blockIdx.x / per_seq;
+  const int rem = blockIdx.x - seq * per_seq;
+  const int tile = rem / p.qruns;
+  const int t0 = (rem - tile * p.qruns) * IBK_QRUN;
+  const int s0 = tile * IB_TILE;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int l15 = lane & 15, g4 = lane >> 4;
+  const int l31 = lane & 31, g2 = lane >> 5;
+  const int half = wave & 1, dn0 = 2 * (wave >> 1);
+
+  __shared__ __attribute__((aligned(16))) uint16_t ahi[IB_TILE * IB_LD];  // [key][head]
+  __shared__ __attribute__((aligned(16))) uint16_t alo[IB_TILE * IB_LD];
+  __shared__ __attribute__((aligned(16))) uint16_t qt[128 * IB_LD];       // [dim][head]
+  __shared__ int qlist[IBK_QRUN];
+  __shared__ int sm[IB_THREADS / WAVE];
+  __shared__ float gsh[IB_TILE];
+  __shared__ int lsh[IB_THREADS / WAVE];
+
+  // The queries of this run that see a key of the tile, in index order, and
+  // the sequence's longest visible history (keys at or past it are not read).
+  int n_rel = 0, lmax = 0;
+  for (int base = 0; base < IBK_QRUN; base += IB_THREADS) {
+    const int t = t0 + base + tid;
+    bool rel = false;
+    if (t < a.num_q && a.q_seq[t] == seq) {
+      const int nv = a.q_nvis[t];
+      lmax = max(lmax, nv);
+      rel = nv > s0;
+    }
+    const uint64_t m = __ballot(rel);
+    const int below = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+    if (lane == 0) sm[wave] = __popcll(m);
+    __syncthreads();
+    int before = n_rel;
+    for (int w = 0; w < wave; ++w) before += sm[w];
+    if (rel) qlist[before + below] = t;
+    for (int w = 0; w < IB_THREADS / WAVE; ++w) n_rel += sm[w];
+    __syncthreads();
+  }
+  if (n_rel == 0) return;  // block-uniform
+  // Keys at or past the longest history among the run's queries of this
+  // sequence are seen by none of them (and may not exist in the cache).
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) lmax = max(lmax, __shfl_xor(lmax, m, WAVE));
+  if (lane == 0) lsh[wave] = lmax;
+  __syncthreads();
+  const int lseq = max(max(lsh[0], lsh[1]), max(lsh[2], lsh[3]));  // > s0
+
+  // The tile's keys as the A operand (every wavefront holds all 64): key
+  // 16 mt + l15, bytes [32 g4, +32).  Keys at or past lseq read key s0 (their
+  // g is 0 for every query of the run, so they gather nothing).
+  v8i ka[4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+    const int pos = s0 + 16 * mt + l15;
+    const int64_t row = phys_row(a.map, seq, pos < lseq ? pos : s0);
+    ka[mt] = load32(a.k8 + row * 128 + 32 * g4);
+  }
+
+  v16f acc[2];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[nt][r] = 0.0f;
+
+  // Per-query operands, one query ahead: this wavefront's 16 heads of q8, the
+  // head's e_j, and (threads 0..63) g of one key of the tile.
+  auto load_q = [&](int i, v8i &qb, float &ej, float &gk) {
+    const int t = qlist[min(i, n_rel - 1)];
+    const int j = 16 * wave + l15;
+    qb = load32(a.q8 + (int64_t)t * (64 * 128) + j * 128 + 32 * g4);
+    const float qs = a.q_scale ? a.q_scale[(int64_t)t * 64 + j] : 1.0f;
+    ej = a.w[(int64_t)t * 64 + j] * qs;
+    const int nv = a.q_nvis[t];
+    const int pos = s0 + (tid & (IB_TILE - 1));
+    gk = (tid < IB_TILE && pos < nv) ? a.grad[(int64_t)t * a.ld_grad + pos] : 0.0f;
+  };
+  v8i qb0, qb1;
+  float e0, e1, g0, g1;
+  load_q(0, qb0, e0, g0);
+
+  auto one_query = [&](const v8i &qb, float ej, float gk) {
+    __syncthreads();  // the previous query's fragment reads are done
+    if (tid < IB_TILE) gsh[tid] = gk;
+    const int j = 16 * wave + l15;
+    // q8 of head j as bf16, transposed: qt[dim][head].
+    const uint32_t qw[8] = {(uint32_t)qb[0], (uint32_t)qb[1], (uint32_t)qb[2], (uint32_t)qb[3],
+                            (uint32_t)qb[4], (uint32_t)qb[5], (uint32_t)qb[6], (uint32_t)qb[7]};
+#pragma unroll
+    for (int wd = 0; wd < 8; ++wd) {
+      float qv[4];
+      fp8x4(qw[wd], qv);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) qt[(32 * g4 + 4 * wd + b) * IB_LD + j] = bf16_bits(qv[b]);
+    }
+    __syncthreads();  // gsh visible
+    // D^T[key][head] for keys 16 mt + 4 g4 + i, head j.
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const v4f d = mfma_fp8_16x16x128(ka[mt], qb, v4f{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = 16 * mt + 4 * g4 + i;
+        const float x = d[i] > 0.0f ? ej * gsh[key] : 0.0f;
+        const uint16_t hi = bf16_bits(x);
+        ahi[key * IB_LD + j] = hi;
+        alo[key * IB_LD + j] = bf16_bits(x - bf16_value(hi));
+      }
+    }
+    __syncthreads();  // a and q8^T visible
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int ao = (32 * half + l31) * IB_LD + 16 * ks + 8 * g2;
+      const uint4 ah = *reinterpret_cast<const uint4 *>(&ahi[ao]);
+      const uint4 al = *reinterpret_cast<const uint4 *>(&alo[ao]);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const uint4 b = *reinterpret_cast<const uint4 *>(&qt[(32 * (dn0 + nt) + l31) * IB_LD + 16 * ks + 8 * g2]);
+        acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(ah), as_bf8(b), acc[nt], 0, 0, 0);
+        acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(al), as_bf8(b), acc[nt], 0, 0, 0);
+      }
+    }
+  };
+  int i = 0;
+  for (; i + 1 < n_rel; i += 2) {
+    load_q(i + 1, qb1, e1, g1);
+    one_query(qb0, e0, g0);
+    load_q(i + 2, qb0, e0, g0);
+    one_query(qb1, e1, g1);
+  }
+  if (i < n_rel) one_query(qb0, e0, g0);
+
+  // acc register r holds key 32 half + 8 (r >> 2) + 4 g2 + (r & 3), dim 32 (dn0 + nt) + l31.
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int pos = s0 + 32 * half + 8 * (r >> 2) + 4 * g2 + (r & 3);
+    if (pos < lseq) {
+      float *dst = a.dk + phys_row(a.map, seq, pos) * 128 + 32 * dn0 + l31;
+      unsafeAtomicAdd(dst, acc[0][r]);
+      unsafeAtomicAdd(dst + 32, acc[1][r]);
+    }
+  }
+}
+
 hipError_t launch_indexer_bwd(const IndexerBwdLaunch &a, int max_set, hipStream_t st) {
   if (a.num_q == 0) return hipSuccess;
   const int64_t nz = (int64_t)a.num_q * 64 * 128;
@@ -324,7 +499,21 @@ hipError_t launch_indexer_bwd(const IndexerBwdLaunch &a, int max_set, hipStream_
   while (members > IB_TILE && (int64_t)a.num_q * chunks(members) < IB_MIN_BLOCKS) members /= 2;
   p.members = members;
   p.nchunk = chunks(members);
-  hipLaunchKernelGGL(indexer_bwd_kernel, dim3((unsigned)((int64_t)a.num_q * p.nchunk)), dim3(IB_THREADS), 0, st, p);
+  const dim3 grid((unsigned)((int64_t)a.num_q * p.nchunk));
+  if (a.idx) {
+    hipLaunchKernelGGL(indexer_bwd_kernel<true>, grid, dim3(IB_THREADS), 0, st, p);
+    return hipGetLastError();
+  }
+  // Dense: dq and dw query-major, dk key-major.
+  hipLaunchKernelGGL(indexer_bwd_kernel<false>, grid, dim3(IB_THREADS), 0, st, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  IndexerBwdDkArgs pk;
+  pk.a = a;
+  pk.tiles = (max_set + IB_TILE - 1) / IB_TILE;
+  pk.qruns = (a.num_q + IBK_QRUN - 1) / IBK_QRUN;
+  const int64_t blocks = (int64_t)a.num_seqs * pk.tiles * pk.qruns;
+  hipLaunchKernelGGL(indexer_bwd_dk_kernel, dim3((unsigned)blocks), dim3(IB_THREADS), 0, st, pk);
   return hipGetLastError();
 }
 
