@@ -350,12 +350,14 @@ __global__ __launch_bounds__(IB_THREADS) void indexer_bwd_dk_kernel(IndexerBwdDk
   const int l31 = lane & 31, g2 = lane >> 5;
   const int half = wave & 1, dn0 = 2 * (wave >> 1);
 
-  __shared__ __attribute__((aligned(16))) uint16_t ahi[IB_TILE * IB_LD];  // [key][head]
-  __shared__ __attribute__((aligned(16))) uint16_t alo[IB_TILE * IB_LD];
-  __shared__ __attribute__((aligned(16))) uint16_t qt[128 * IB_LD];       // [dim][head]
+  // Two sets, alternating between queries: query i writes set i & 1 while
+  // slower wavefronts may still read set (i - 1) & 1, so one barrier per
+  // query suffices.
+  __shared__ __attribute__((aligned(16))) uint16_t ahi[2][IB_TILE * IB_LD];  // [key][head]
+  __shared__ __attribute__((aligned(16))) uint16_t alo[2][IB_TILE * IB_LD];
+  __shared__ __attribute__((aligned(16))) uint16_t qt[2][128 * IB_LD];       // [dim][head]
   __shared__ int qlist[IBK_QRUN];
   __shared__ int sm[IB_THREADS / WAVE];
-  __shared__ float gsh[IB_TILE];
   __shared__ int lsh[IB_THREADS / WAVE];
 
   // The queries of this run that see a key of the tile, in index order, and
@@ -406,71 +408,82 @@ __global__ __launch_bounds__(IB_THREADS) void indexer_bwd_dk_kernel(IndexerBwdDk
     for (int r = 0; r < 16; ++r) acc[nt][r] = 0.0f;
 
   // Per-query operands, one query ahead: this wavefront's 16 heads of q8, the
-  // head's e_j, and (threads 0..63) g of one key of the tile.
-  auto load_q = [&](int i, v8i &qb, float &ej, float &gk) {
+  // head's e_j, and g of the 16 keys whose D values this lane holds (keys
+  // 16 mt + 4 g4 + i; 0 past the query's history).
+  struct QueryOps {
+    v8i qb;
+    float e;
+    float g[16];
+  };
+  auto load_q = [&](int i, QueryOps &o) {
     const int t = qlist[min(i, n_rel - 1)];
     const int j = 16 * wave + l15;
-    qb = load32(a.q8 + (int64_t)t * (64 * 128) + j * 128 + 32 * g4);
+    o.qb = load32(a.q8 + (int64_t)t * (64 * 128) + j * 128 + 32 * g4);
     const float qs = a.q_scale ? a.q_scale[(int64_t)t * 64 + j] : 1.0f;
-    ej = a.w[(int64_t)t * 64 + j] * qs;
+    o.e = a.w[(int64_t)t * 64 + j] * qs;
     const int nv = a.q_nvis[t];
-    const int pos = s0 + (tid & (IB_TILE - 1));
-    gk = (tid < IB_TILE && pos < nv) ? a.grad[(int64_t)t * a.ld_grad + pos] : 0.0f;
+    const float *gr = a.grad + (int64_t)t * a.ld_grad;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i2 = 0; i2 < 4; ++i2) {
+        const int pos = s0 + 16 * mt + 4 * g4 + i2;
+        o.g[4 * mt + i2] = pos < nv ? gr[pos] : 0.0f;
+      }
   };
-  v8i qb0, qb1;
-  float e0, e1, g0, g1;
-  load_q(0, qb0, e0, g0);
 
-  auto one_query = [&](const v8i &qb, float ej, float gk) {
-    __syncthreads();  // the previous query's fragment reads are done
-    if (tid < IB_TILE) gsh[tid] = gk;
+  auto one_query = [&](const QueryOps &o, const int set) {
     const int j = 16 * wave + l15;
+    uint16_t *qts = qt[set];
+    uint16_t *ah = ahi[set];
+    uint16_t *al = alo[set];
     // q8 of head j as bf16, transposed: qt[dim][head].
-    const uint32_t qw[8] = {(uint32_t)qb[0], (uint32_t)qb[1], (uint32_t)qb[2], (uint32_t)qb[3],
-                            (uint32_t)qb[4], (uint32_t)qb[5], (uint32_t)qb[6], (uint32_t)qb[7]};
+    const uint32_t qw[8] = {(uint32_t)o.qb[0], (uint32_t)o.qb[1], (uint32_t)o.qb[2], (uint32_t)o.qb[3],
+                            (uint32_t)o.qb[4], (uint32_t)o.qb[5], (uint32_t)o.qb[6], (uint32_t)o.qb[7]};
 #pragma unroll
     for (int wd = 0; wd < 8; ++wd) {
       float qv[4];
       fp8x4(qw[wd], qv);
 #pragma unroll
-      for (int b = 0; b < 4; ++b) qt[(32 * g4 + 4 * wd + b) * IB_LD + j] = bf16_bits(qv[b]);
+      for (int b = 0; b < 4; ++b) qts[(32 * g4 + 4 * wd + b) * IB_LD + j] = bf16_bits(qv[b]);
     }
-    __syncthreads();  // gsh visible
-    // D^T[key][head] for keys 16 mt + 4 g4 + i, head j.
+    // D^T[key][head] for keys 16 mt + 4 g4 + i, head j; a = [D > 0] e_j g_s.
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      const v4f d = mfma_fp8_16x16x128(ka[mt], qb, v4f{0.f, 0.f, 0.f, 0.f});
+      const v4f d = mfma_fp8_16x16x128(ka[mt], o.qb, v4f{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int key = 16 * mt + 4 * g4 + i;
-        const float x = d[i] > 0.0f ? ej * gsh[key] : 0.0f;
+        const float x = d[i] > 0.0f ? o.e * o.g[4 * mt + i] : 0.0f;
         const uint16_t hi = bf16_bits(x);
-        ahi[key * IB_LD + j] = hi;
-        alo[key * IB_LD + j] = bf16_bits(x - bf16_value(hi));
+        ah[key * IB_LD + j] = hi;
+        al[key * IB_LD + j] = bf16_bits(x - bf16_value(hi));
       }
     }
-    __syncthreads();  // a and q8^T visible
+    __syncthreads();  // this query's a and q8^T visible
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int ao = (32 * half + l31) * IB_LD + 16 * ks + 8 * g2;
-      const uint4 ah = *reinterpret_cast<const uint4 *>(&ahi[ao]);
-      const uint4 al = *reinterpret_cast<const uint4 *>(&alo[ao]);
+      const uint4 fh = *reinterpret_cast<const uint4 *>(&ah[ao]);
+      const uint4 fl = *reinterpret_cast<const uint4 *>(&al[ao]);
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
-        const uint4 b = *reinterpret_cast<const uint4 *>(&qt[(32 * (dn0 + nt) + l31) * IB_LD + 16 * ks + 8 * g2]);
-        acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(ah), as_bf8(b), acc[nt], 0, 0, 0);
-        acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(al), as_bf8(b), acc[nt], 0, 0, 0);
+        const uint4 b = *reinterpret_cast<const uint4 *>(&qts[(32 * (dn0 + nt) + l31) * IB_LD + 16 * ks + 8 * g2]);
+        acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(fh), as_bf8(b), acc[nt], 0, 0, 0);
+        acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(fl), as_bf8(b), acc[nt], 0, 0, 0);
       }
     }
   };
+  QueryOps o0, o1;
+  load_q(0, o0);
   int i = 0;
   for (; i + 1 < n_rel; i += 2) {
-    load_q(i + 1, qb1, e1, g1);
-    one_query(qb0, e0, g0);
-    load_q(i + 2, qb0, e0, g0);
-    one_query(qb1, e1, g1);
+    load_q(i + 1, o1);
+    one_query(o0, 0);
+    load_q(i + 2, o0);
+    one_query(o1, 1);
   }
-  if (i < n_rel) one_query(qb0, e0, g0);
+  if (i < n_rel) one_query(o0, 0);
 
   // acc register r holds key 32 half + 8 (r >> 2) + 4 g2 + (r & 3), dim 32 (dn0 + nt) + l31.
 #pragma unroll
