@@ -551,6 +551,12 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
 }
 
 // Merge split partials: out = sum_s exp(lse_s - M) O_s / sum_s exp(lse_s - M).
+// NS > 0 fixes the split count at compile time, so that every partial's lse
+// and value are requested before the first is used (one memory round trip
+// instead of one per split); NS = 0 takes any count.  A split with no row
+// (lse = -inf) has weight 0 and a zero partial; all splits empty gives 0 and
+// lse = -inf.
+template <int NS>
 __global__ __launch_bounds__(256) void mla_combine_kernel(const float *__restrict__ part_o,
                                                           const float *__restrict__ part_lse, int nsplit, int num_q,
                                                           float *__restrict__ out, float *__restrict__ lse) {
@@ -561,18 +567,36 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const float *__restric
   const int head = 2 * (y & 63) + (threadIdx.x >> 7);
   const int d = 4 * (threadIdx.x & 127);
   const float *pl = part_lse + (int64_t)q * nsplit * 128 + head;
-  float mx = -INFINITY;
-  for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, pl[s * 128]);
+  const float *po = part_o + ((int64_t)q * nsplit * 128 + head) * 512 + d;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  float den = 0.0f;
-  if (mx != -INFINITY) {
-    for (int s = 0; s < nsplit; ++s) {
-      const float ls = pl[s * 128];
-      if (ls == -INFINITY) continue;
-      const float wgt = expf(ls - mx);
-      const float4 v = *reinterpret_cast<const float4 *>(part_o + (((int64_t)q * nsplit + s) * 128 + head) * 512 + d);
-      acc.x += wgt * v.x; acc.y += wgt * v.y; acc.z += wgt * v.z; acc.w += wgt * v.w;
+  float den = 0.0f, mx = -INFINITY;
+  if (NS > 0) {
+    float ls[NS > 0 ? NS : 1];
+    float4 v[NS > 0 ? NS : 1];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      ls[s] = pl[s * 128];
+      v[s] = *reinterpret_cast<const float4 *>(po + (int64_t)s * 128 * 512);
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s) mx = fmaxf(mx, ls[s]);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const float wgt = (ls[s] == -INFINITY) ? 0.0f : expf(ls[s] - mx);
+      acc.x += wgt * v[s].x; acc.y += wgt * v[s].y; acc.z += wgt * v[s].z; acc.w += wgt * v[s].w;
       den += wgt;
+    }
+  } else {
+    for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, pl[s * 128]);
+    if (mx != -INFINITY) {
+      for (int s = 0; s < nsplit; ++s) {
+        const float ls = pl[s * 128];
+        if (ls == -INFINITY) continue;
+        const float wgt = expf(ls - mx);
+        const float4 v = *reinterpret_cast<const float4 *>(po + (int64_t)s * 128 * 512);
+        acc.x += wgt * v.x; acc.y += wgt * v.y; acc.z += wgt * v.z; acc.w += wgt * v.w;
+        den += wgt;
+      }
     }
   }
   const float inv = den > 0.0f ? 1.0f / den : 0.0f;
@@ -655,8 +679,24 @@ hipError_t launch_mla(const MlaLaunch &a, bool decode, void *ws, hipStream_t st)
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.nsplit == 1) return e;
-  hipLaunchKernelGGL(mla_combine_kernel, dim3((unsigned)(nq8 * 64)), dim3(256), 0, st, p.part_o, p.part_lse,
-                     p.nsplit, a.num_q, a.out, a.lse);
+  const dim3 cgrid((unsigned)(nq8 * 64));
+  switch (p.nsplit) {
+    case 2:
+      hipLaunchKernelGGL(mla_combine_kernel<2>, cgrid, dim3(256), 0, st, p.part_o, p.part_lse, 2, a.num_q, a.out, a.lse);
+      break;
+    case 3:
+      hipLaunchKernelGGL(mla_combine_kernel<3>, cgrid, dim3(256), 0, st, p.part_o, p.part_lse, 3, a.num_q, a.out, a.lse);
+      break;
+    case 4:
+      hipLaunchKernelGGL(mla_combine_kernel<4>, cgrid, dim3(256), 0, st, p.part_o, p.part_lse, 4, a.num_q, a.out, a.lse);
+      break;
+    case 8:
+      hipLaunchKernelGGL(mla_combine_kernel<8>, cgrid, dim3(256), 0, st, p.part_o, p.part_lse, 8, a.num_q, a.out, a.lse);
+      break;
+    default:
+      hipLaunchKernelGGL(mla_combine_kernel<0>, cgrid, dim3(256), 0, st, p.part_o, p.part_lse, p.nsplit, a.num_q,
+                         a.out, a.lse);
+  }
   return hipGetLastError();
 }
 

@@ -33,12 +33,19 @@ __device__ __forceinline__ v8bf as_bf(const uint4 &u) { return __builtin_bit_cas
 // Tile layout in LDS.  The 32 rows x 72 chunks (16 bytes) of a tile are
 // stored in four 9216-byte groups of 8 rows; inside a group, chunk block
 // c >> 3 (9 blocks of 1 KiB) holds the 8 rows x 8 chunks as [row & 7][slot],
-// slot = (c & 7) ^ (r & 7) ^ ((r >> 3) & 1).  A gather instruction then fills
-// one contiguous 1 KiB block (lane l: row l >> 3, slot l & 7) and each lane
-// reads a single cache row per tile; the XOR spreads the 16 rows that one
-// 16-byte read instruction serves per cycle over all 16 bank groups.
+// slot = (c & 7) ^ row_xor(r).  A gather instruction then fills one
+// contiguous 1 KiB block (lane l: row l >> 3, slot l & 7) and each lane reads
+// a single cache row per tile.  With 64 four-byte banks, a 16-byte slot of
+// row r starts in bank group 8 * (r & 1) + slot, and row_xor is chosen so
+// that both read patterns hit 16 different groups:
+//  * the QK read (16 lanes per cycle: 16 consecutive rows, one chunk) needs
+//    row_xor to be a permutation over the 8 even and over the 8 odd rows;
+//  * the transposing PV read (32 lanes per cycle: rows 4j .. 4j+3 of a
+//    group, chunks 4m .. 4m+3) needs rows r and r + 2 of each such set to
+//    differ in bit 2, which the chunks (bits 0-1) cannot reach.
+__device__ __forceinline__ int row_xor(int r) { return (r & 7) ^ ((r >> 3) & 1) ^ (((r >> 1) & 1) << 2); }
 __device__ __forceinline__ int tile_off(int r, int c) {
-  return 9216 * (r >> 3) + 1024 * (c >> 3) + 128 * (r & 7) + 16 * ((c & 7) ^ (r & 7) ^ ((r >> 3) & 1));
+  return 9216 * (r >> 3) + 1024 * (c >> 3) + 128 * (r & 7) + 16 * ((c & 7) ^ row_xor(r));
 }
 
 // S^T chain of the QK product on a VGPR accumulator.  Written as asm
@@ -62,8 +69,8 @@ __device__ __forceinline__ void mfma_s_drain(v16f &acc) {
 
 // Gathers this wavefront's share of the tile whose first row is prow entry r0:
 // tile rows 8*wave .. 8*wave+7, lane l taking row l >> 3 and, in part i,
-// chunk 8*i + ((l & 7) ^ (l >> 3) ^ (wave & 1)), into 1 KiB block i of the
-// wavefront's 8-row group (see tile_off).  When `real` is false the parts
+// chunk 8*i + ((l & 7) ^ row_xor(8*wave + (l >> 3))), into 1 KiB block i of
+// the wavefront's 8-row group (see tile_off).  When `real` is false the parts
 // read the block's first row into the (free) buffer instead, so the caller's
 // instruction stream has no branch.
 //
@@ -90,7 +97,7 @@ __device__ __forceinline__ uint32_t tile_row(const uint32_t *prow, int r0, bool 
 template <bool WIDE>
 __device__ __forceinline__ void issue_part(const __amdgpu_buffer_rsrc_t rs, const uint16_t *__restrict__ kv,
                                            uint32_t brow, uint32_t row, uint8_t *buf, int wave, int lane, int i) {
-  const int cx = (lane & 7) ^ (lane >> 3) ^ (wave & 1);
+  const int cx = (lane & 7) ^ row_xor(8 * wave + (lane >> 3));
   uint8_t *dst = buf + 9216 * wave + 1024 * i;
   if (WIDE) {
     const uint16_t *src = kv + (size_t)row * 576 + 8 * cx + 64 * i;
