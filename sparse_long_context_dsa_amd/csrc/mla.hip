@@ -144,6 +144,10 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
   // Selected positions -> physical rows.  A position outside [0, n_vis) breaks
   // the contract; it is loaded from position 0 (in bounds, finite) and masked.
   const int seq = a.q_seq[q];
+  // A contiguous cache's first row of the sequence, loaded before the q
+  // fragments: loads complete in issue order, so waiting for a later one
+  // would also wait for all of q.
+  const uint32_t row0 = a.map.block_shift < 0 ? (uint32_t)a.map.seq_row0[seq] : 0u;
   // All of a thread's positions, and then their block-table entries, are
   // loaded before any is used, every lane issuing the same loads (indices
   // clamped into range, no branch), so they overlap instead of taking one
@@ -152,20 +156,33 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
   constexpr int PER_THREAD_T = (MLA_MAX_ROWS + MLA_T + MLA_THREADS - 1) / MLA_THREADS;
   const bool dense = p.dense != 0;
   int bad = 0;
+  // Queries of this wavefront's own 32 heads: B fragments of S^T = K . Q^T.
+  // Requested right after the block's first position (or block-table) loads
+  // and before those values are used, so that their latency overlaps the
+  // position -> row lookup and the first gathers.  A block with no rows
+  // never reads them.
+  uint4 qb[36];
+  auto load_q = [&]() {
+    const uint16_t *qr = a.q + ((int64_t)q * 128 + 32 * wave + c) * 576 + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < 36; ++ks) qb[ks] = *reinterpret_cast<const uint4 *>(qr + 16 * ks);
+  };
   if (dense && nrows > 0) {  // block-uniform
     // Dense: the base row of each 32-row tile of positions r0, r0 + 32, ...
     const int nt = (nrows + MLA_T - 1) / MLA_T;  // <= MLA_MAX_ROWS + MLA_T (the launcher splits longer rows)
     uint32_t base[PER_THREAD_T];
     if (a.map.block_shift < 0) {
-      const uint32_t s0 = (uint32_t)a.map.seq_row0[seq] + (uint32_t)r0;
+      const uint32_t s0 = row0 + (uint32_t)r0;
 #pragma unroll
       for (int j = 0; j < PER_THREAD_T; ++j) base[j] = s0 + (uint32_t)(MLA_T * (tid + j * MLA_THREADS));
+      load_q();
     } else {
       const int32_t *bt = a.map.block_table + (int64_t)seq * a.map.max_blocks;
       const int sh = a.map.block_shift;
       int32_t blk[PER_THREAD_T];
 #pragma unroll
       for (int j = 0; j < PER_THREAD_T; ++j) blk[j] = bt[(r0 + MLA_T * min(tid + j * MLA_THREADS, nt - 1)) >> sh];
+      load_q();
 #pragma unroll
       for (int j = 0; j < PER_THREAD_T; ++j) {
         const int pos = r0 + MLA_T * min(tid + j * MLA_THREADS, nt - 1);
@@ -180,6 +197,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
     int pos[PER_THREAD];
 #pragma unroll
     for (int j = 0; j < PER_THREAD; ++j) pos[j] = ip[min(tid + j * MLA_THREADS, nrows - 1)];
+    load_q();
     bool ok[PER_THREAD];
 #pragma unroll
     for (int j = 0; j < PER_THREAD; ++j) {
@@ -188,9 +206,8 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
     }
     uint32_t row[PER_THREAD];
     if (a.map.block_shift < 0) {  // contiguous
-      const uint32_t r0 = (uint32_t)a.map.seq_row0[seq];
 #pragma unroll
-      for (int j = 0; j < PER_THREAD; ++j) row[j] = r0 + (uint32_t)pos[j];
+      for (int j = 0; j < PER_THREAD; ++j) row[j] = row0 + (uint32_t)pos[j];
     } else {  // paged
       const int32_t *bt = a.map.block_table + (int64_t)seq * a.map.max_blocks;
       const int sh = a.map.block_shift;
@@ -242,24 +259,29 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
     for (int half = 0; half < 2; ++half)
       tr_base[odd][half] = tile_off(8 * half + 4 * g + tr_r, 4 * odd + tr_x) + 8 * tr_piece;
 
-  // prow ready; does any row need masking beyond a partial last tile?
-  const bool any_bad = __syncthreads_or(bad) != 0;
+  // prow ready; does any row need masking beyond a partial last tile?  One
+  // LDS word per wavefront and a bare barrier: __syncthreads_or would also
+  // wait for every outstanding load, the q fragments included, before the
+  // first gathers could be issued.
+  __shared__ int bad_w[MLA_WAVES];
+  {
+    const int wbad = __ballot(bad) != 0ull ? 1 : 0;
+    if (lane == 0) bad_w[wave] = wbad;
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): prow and bad_w written
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  }
+  const bool any_bad = (bad_w[0] | bad_w[1] | bad_w[2] | bad_w[3]) != 0;
+  static_assert(MLA_WAVES == 4, "any_bad reads four wavefront words");
   const int ntiles = (nrows + MLA_T - 1) / MLA_T;
   // Buffer descriptor of the latent cache from row brow on.
   const uint32_t brow = __builtin_amdgcn_readfirstlane(
-      (!WIDE && a.map.block_shift < 0) ? (uint32_t)a.map.seq_row0[seq] : 0u);
+      (!WIDE && a.map.block_shift < 0) ? row0 : 0u);
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t *>(a.kv + (size_t)brow * 576), (short)0, 0xFFFFFFFF, 0x00020000);
   if (ntiles > 0) issue_tile<WIDE>(rs, a.kv, brow, prow, 0, true, nrows - 1, dense, tb0, wave, lane);
   if (!PIPE && ntiles > 1) issue_tile<WIDE>(rs, a.kv, brow, prow, MLA_T, true, nrows - 1, dense, tb1, wave, lane);
-  // Queries of this wavefront's own 32 heads: B fragments of S^T = K . Q^T,
-  // loaded while the first two tiles are gathered.
-  uint4 qb[36];
-  {
-    const uint16_t *qr = a.q + ((int64_t)q * 128 + head) * 576 + 8 * g;
-#pragma unroll
-    for (int ks = 0; ks < 36; ++ks) qb[ks] = *reinterpret_cast<const uint4 *>(qr + 16 * ks);
-  }
 
   // ---- One tile, in pieces shared by the two schedules below. ----
   auto no_hook = [](int) {};
@@ -534,6 +556,9 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
     lbase = p.part_lse + ((int64_t)q * p.nsplit + sp) * 128;
   }
   // Each value is scaled by its head's 1/l on its way out of the AGPRs.
+  // (256 KiB of O per workgroup: the CU's store bandwidth bounds this, not
+  // the instruction count; staging through LDS for 16-byte stores measured
+  // slower.)
   {
     float il[16];
     read_head_values(iex[wave], g, il);
