@@ -82,9 +82,22 @@ __global__ __launch_bounds__(MLA_THREADS, 2) void kl_target_kernel(KlTargetArgs 
   __shared__ float red[MLA_WAVES][MLA_T];  // per-wavefront head sums of one tile
 
   // Members -> physical rows: every lane issues the same loads (indices
-  // clamped into range) before any is used.
+  // clamped into range) before any is used.  Loads complete in issue order:
+  // the sequence's first row comes first, the q fragments and the head's
+  // log-sum-exp right after the positions and before those are used, so no
+  // later wait (nor the row table's barrier, a bare one) holds the first
+  // gathers back behind all of q.
   const int seq = a.q_seq[q];
+  const uint32_t row0 = a.map.block_shift < 0 ? (uint32_t)a.map.seq_row0[seq] : 0u;
   int bad = 0;
+  uint4 qb[36];
+  float lse_h;
+  auto load_q = [&]() {
+    lse_h = a.lse[(int64_t)q * 128 + head];
+    const uint16_t *qr = a.q + ((int64_t)q * 128 + head) * 576 + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < 36; ++ks) qb[ks] = *reinterpret_cast<const uint4 *>(qr + 16 * ks);
+  };
   {
     int pos[KLT_PER_THREAD];
     if (a.idx) {
@@ -95,6 +108,7 @@ __global__ __launch_bounds__(MLA_THREADS, 2) void kl_target_kernel(KlTargetArgs 
 #pragma unroll
       for (int j = 0; j < KLT_PER_THREAD; ++j) pos[j] = r0 + min(tid + j * MLA_THREADS, nrows - 1);
     }
+    load_q();
     bool ok[KLT_PER_THREAD];
 #pragma unroll
     for (int j = 0; j < KLT_PER_THREAD; ++j) {
@@ -103,9 +117,8 @@ __global__ __launch_bounds__(MLA_THREADS, 2) void kl_target_kernel(KlTargetArgs 
     }
     uint32_t row[KLT_PER_THREAD];
     if (a.map.block_shift < 0) {
-      const uint32_t s0 = (uint32_t)a.map.seq_row0[seq];
 #pragma unroll
-      for (int j = 0; j < KLT_PER_THREAD; ++j) row[j] = s0 + (uint32_t)pos[j];
+      for (int j = 0; j < KLT_PER_THREAD; ++j) row[j] = row0 + (uint32_t)pos[j];
     } else {
       const int32_t *bt = a.map.block_table + (int64_t)seq * a.map.max_blocks;
       const int sh = a.map.block_shift;
@@ -125,11 +138,20 @@ __global__ __launch_bounds__(MLA_THREADS, 2) void kl_target_kernel(KlTargetArgs 
       }
     }
   }
-  const bool any_bad = __syncthreads_or(bad) != 0;
+  __shared__ int bad_w[MLA_WAVES];
+  {
+    const int wbad = __ballot(bad) != 0ull ? 1 : 0;
+    if (lane == 0) bad_w[wave] = wbad;
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): prow and bad_w written
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  }
+  static_assert(MLA_WAVES == 4, "any_bad reads four wavefront words");
+  const bool any_bad = (bad_w[0] | bad_w[1] | bad_w[2] | bad_w[3]) != 0;
 
   const int ntiles = (nrows + MLA_T - 1) / MLA_T;
-  const uint32_t brow = __builtin_amdgcn_readfirstlane(
-      (!WIDE && a.map.block_shift < 0) ? (uint32_t)a.map.seq_row0[seq] : 0u);
+  const uint32_t brow = __builtin_amdgcn_readfirstlane((!WIDE && a.map.block_shift < 0) ? row0 : 0u);
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t *>(a.kv + (size_t)brow * 576), (short)0, 0xFFFFFFFF, 0x00020000);
   issue_tile<WIDE>(rs, a.kv, brow, prow, 0, true, nrows - 1, false, tb0, wave, lane);
@@ -137,15 +159,7 @@ __global__ __launch_bounds__(MLA_THREADS, 2) void kl_target_kernel(KlTargetArgs 
 
   // The head's log-sum-exp in log2 units, negated; a head with no finite
   // log-sum-exp contributes nothing.
-  const float lse_h = a.lse[(int64_t)q * 128 + head];
   const float nl = (lse_h > -INFINITY && lse_h < INFINITY) ? -lse_h * LOG2E : -INFINITY;
-  // Queries of this wavefront's 32 heads: B fragments of S^T = K . Q^T.
-  uint4 qb[36];
-  {
-    const uint16_t *qr = a.q + ((int64_t)q * 128 + head) * 576 + 8 * g;
-#pragma unroll
-    for (int ks = 0; ks < 36; ++ks) qb[ks] = *reinterpret_cast<const uint4 *>(qr + 16 * ks);
-  }
 
   // QK: lane reads row c, chunk 2*ks + g of the tile.
   int qk_base[4];
