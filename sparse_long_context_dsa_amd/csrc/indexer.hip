@@ -23,7 +23,8 @@
 // are clamped, not skipped), and the block-table lookups are done once before
 // the loop, so the waits on the prefetch count exactly the loads they need.  ReLU, the weighting and 16 of the 64 head
 // terms are summed in-lane; the remaining 4-way sum across lane groups is a
-// butterfly that also transposes, so lane l ends with the score of key s0+l.
+// butterfly of vector-ALU lane swaps (v_permlane32_swap, v_permlane16_swap)
+// that also transposes, so lane l ends with the score of key s0+l.
 // Scores of four steps are staged in LDS and leave as 16-byte stores (1 KiB
 // per wavefront instruction).
 //
@@ -65,6 +66,18 @@ __device__ __forceinline__ void load_step(const IndexerLaunch &a, int64_t base, 
   st.ks = E8M0 ? e8m0_value(a.k_e8m0[base + min(lane, last)]) : a.k_scale[base + min(lane, last)];
 }
 
+// a from this lane plus the partner value that v_permlane{16,32}_swap brings
+// in: with vdst = a and src0 = b, the swap exchanges the upper half (16 or 32
+// lanes) of a with the lower half of b, so each lane's two results are its
+// own and its partner's (lane ^ 16 or lane ^ 32) copy of the same operand --
+// a for lanes in the lower half, b for lanes in the upper half.
+template <bool SWAP16>
+__device__ __forceinline__ float swap_sum(float a, float b) {
+  const auto r = SWAP16 ? __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false)
+                        : __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ float relu(float x) {
   float r;
   asm("v_max_f32 %0, 0, %1" : "=v"(r) : "v"(x));  // one instruction, no canonicalize
@@ -72,7 +85,12 @@ __device__ __forceinline__ float relu(float x) {
 }
 
 template <bool HIST, bool E8M0>
-__global__ __launch_bounds__(256) void indexer_kernel(IndexerLaunch a, int nchunks, int kpw) {
+// Three wavefronts per SIMD: the epilogue of key tile t overlapping tile
+// t + 1's MFMAs needs 16 more registers than a serial epilogue, and left to
+// itself the compiler would spend them on accumulator registers and drop to
+// two wavefronts.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void indexer_kernel(IndexerLaunch a,
+                                                                                               int nchunks, int kpw) {
   const int q = blockIdx.x / nchunks;
   const int chunk = blockIdx.x - q * nchunks;
   const int nvis = a.q_nvis[q];
@@ -111,8 +129,6 @@ __global__ __launch_bounds__(256) void indexer_kernel(IndexerLaunch a, int nchun
   const int s_begin = (chunk * IDX_WAVES + wave) * kpw;
   const int s_end = min(s_begin + kpw, nvis);
   float *srow = a.scores + (int64_t)q * a.ld;
-  const int g = lane >> 4;
-  const bool b1 = (g & 2) != 0, b0 = (g & 1) != 0;
 
   // Physical row of each 64-key step of this wavefront's run (a step never
   // straddles a cache block), one step per lane, looked up once: the loop then
@@ -153,24 +169,34 @@ __global__ __launch_bounds__(256) void indexer_kernel(IndexerLaunch a, int nchun
       pending = -1;
     }
     float p[4];
+    // The MFMAs of key tile t + 1 are issued before the epilogue of tile t,
+    // so the matrix core works while the vector ALU weights tile t's heads.
+    v4f c[2][4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) c[0][mt] = mfma_fp8_16x16x128(A[mt], cur.b[0], v4f{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
+      if (t + 1 < 4) {
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          c[(t + 1) & 1][mt] = mfma_fp8_16x16x128(A[mt], cur.b[t + 1], v4f{0.f, 0.f, 0.f, 0.f});
+      }
+      __builtin_amdgcn_sched_barrier(0);
       float acc_sum = 0.0f;
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const v4f c = mfma_fp8_16x16x128(A[mt], cur.b[t], v4f{0.f, 0.f, 0.f, 0.f});
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc_sum = fmaf(coef[mt][r], relu(c[r]), acc_sum);
-      }
+        for (int r = 0; r < 4; ++r) acc_sum = fmaf(coef[mt][r], relu(c[t & 1][mt][r]), acc_sum);
       p[t] = acc_sum;
     }
     // Reduce over the 4 lane groups and scatter: lane group g keeps tile g.
-    const float ra = shfl_xor(b1 ? p[0] : p[2], 32);
-    const float rb = shfl_xor(b1 ? p[1] : p[3], 32);
-    const float x0 = (b1 ? p[2] : p[0]) + ra;
-    const float x1 = (b1 ? p[3] : p[1]) + rb;
-    const float rc = shfl_xor(b0 ? x0 : x1, 16);
-    const float score = ((b0 ? x1 : x0) + rc) * cur.ks;
+    // The lane swaps run on the vector ALU (no LDS round trip): swapping the
+    // upper half of tile t with the lower half of tile t + 2 leaves every lane
+    // with its own and its partner's (lane ^ 32) partial of the tile its half
+    // keeps, in the two results; likewise for lane ^ 16 one level down.
+    const float x0 = swap_sum<false>(p[0], p[2]);
+    const float x1 = swap_sum<false>(p[1], p[3]);
+    const float score = swap_sum<true>(x0, x1) * cur.ks;
     const int j = ((s0 - s_begin) >> 6) & 3;  // step within the 256-key group
     sbuf[wave][64 * j + lane] = score;
     // Lane l stores keys g0 + 4l .. g0 + 4l + 3 of the group.
