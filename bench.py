@@ -41,10 +41,10 @@ CALIB_BYTES = 1 << 30           # size of the calibration copy (read and written
 # same counter reads for the 1 GiB calibration copy.  Valid only for the kernel
 # source it was measured on: the figure is dropped when indexer.hip changes.
 INDEXER_TRAFFIC = {
-    "source_sha": "682c0f559e5d5f7a",
-    "fetch_kib": 543003, "write_kib": 35887,          # raw counter readings
-    "calib_fetch_kib": 524318, "calib_write_kib": 1048576,  # the 1 GiB copy
-    "bytes_per_launch": 1148754802,
+    "source_sha": "96ea35b9badf501a",
+    "fetch_kib": 542966, "write_kib": 35887,          # raw counter readings
+    "calib_fetch_kib": 524294, "calib_write_kib": 1048576,  # the 1 GiB copy
+    "bytes_per_launch": 1148729930,
 }
 
 
