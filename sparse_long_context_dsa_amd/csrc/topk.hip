@@ -249,7 +249,13 @@ struct SelectArgs {
   TopkWs ws;
 };
 
-__global__ __launch_bounds__(TK_THREADS) void topk_row_kernel(SelectArgs a) {
+// Three wavefronts per SIMD (at most 168 VGPRs; the 64 keys per thread take
+// 64): left to itself the compiler used 179 and fit two, and with only two rows
+// per CU in flight the row loads, not the selection, set the pace (prefill
+// top-k 0.60 -> 0.43 ms).  Four per SIMD would need spills, which measured
+// slower.
+__global__ __launch_bounds__(TK_THREADS) __attribute__((amdgpu_waves_per_eu(3, 3))) void topk_row_kernel(
+    SelectArgs a) {
   const int q = blockIdx.x;
   const int n = a.q_nvis[q];
   const int k = a.k;
