@@ -43,16 +43,21 @@
 
 namespace dsa {
 
-constexpr int TK_THREADS = 256;
-constexpr int TK_ROUNDS = 8;                                  // rounds per block
-constexpr int TK_J = TOPK_ROW_MAX / (TK_THREADS * TK_ROUNDS);  // 8 scores per thread per round
-constexpr int TK_PER = TK_ROUNDS * TK_J;                      // 64 keys per thread
-constexpr int TK_ROUND_SPAN = TK_THREADS * TK_J;              // 2048 positions per round
+constexpr int TK_THREADS = 256;                               // threads of a row block
+constexpr int TK_J = 8;                                       // scores per thread per round (two float4)
+// A block of NT threads holding one row of up to TOPK_ROW_MAX scores in
+// registers: ROUNDS rounds of TK_J consecutive scores per thread.
+template <int NT>
+struct RowShape {
+  static constexpr int ROUNDS = TOPK_ROW_MAX / (NT * TK_J);  // 8 for 256 threads, 2 for 1024
+  static constexpr int PER = ROUNDS * TK_J;                  // keys per thread
+  static constexpr int ROUND_SPAN = NT * TK_J;               // positions per round
+  static_assert(ROUNDS >= 1 && ROUNDS <= 8 && ROUNDS * NT * TK_J == TOPK_ROW_MAX, "whole rounds, <= 8");
+};
 constexpr int LONG_THREADS = TOPK_LONG_WAVES * WAVE;
 constexpr int LONG_ROUNDS = TOPK_WAVE_SPAN / 512;  // rounds of 512 positions per wavefront
 constexpr int TAIL_CAP = 12288;                     // candidates the finishing block keeps in LDS
 static_assert(TOPK_CHUNK == TOPK_ROW_MAX, "one histogram block covers one chunk");
-static_assert(TK_J == 8, "two float4 loads per round");
 
 static inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -141,18 +146,22 @@ __device__ __forceinline__ void zero_lds(uint32_t *h, int n) {
 }
 
 // Position of key slot (round rr, element j) of thread t relative to the block start.
-__device__ __forceinline__ int slot_pos(int t, int rr, int j) { return rr * TK_ROUND_SPAN + TK_J * t + j; }
+template <int NT>
+__device__ __forceinline__ int slot_pos(int t, int rr, int j) {
+  return rr * RowShape<NT>::ROUND_SPAN + TK_J * t + j;
+}
 
-// Loads the 64 scores of this thread (positions base + slot_pos).  Positions
+// Loads the scores of this thread (positions base + slot_pos).  Positions
 // >= n get key 0, below the key of any real score (even -inf maps to
 // 0x007FFFFF): key 0 sits in first-digit bin 0, which no real score occupies,
 // so it never reaches a threshold bin, never ties the k-th key and is never
 // selected; the kernels need no separate position test.
+template <int NT>
 __device__ __forceinline__ void load_keys(const float *row, int base, int n, uint32_t *key) {
   const int t = threadIdx.x;
 #pragma unroll
-  for (int rr = 0; rr < TK_ROUNDS; ++rr) {
-    const int i = base + slot_pos(t, rr, 0);
+  for (int rr = 0; rr < RowShape<NT>::ROUNDS; ++rr) {
+    const int i = base + slot_pos<NT>(t, rr, 0);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int ii = i + 4 * h;
@@ -170,34 +179,48 @@ __device__ __forceinline__ void load_keys(const float *row, int base, int n, uin
   }
 }
 
-// Per-round counts (each <= 8) packed 12 bits per round: rounds 0..4 in w0,
-// 5..7 in w1.  Prefixes and totals of a field stay below 4096.
+// Per-round counts (each <= TK_J) packed into two 64-bit words, so that one
+// pair of block scans orders every round.  A field must hold the block total
+// of its round, NT * TK_J: 12-bit fields (5 per word) for 256 threads (2048),
+// 32-bit fields (2 per word) for 1024 threads (8192; 2 rounds).
 struct Packed {
   uint64_t w0, w1;
 };
+template <int NT>
+struct PackShape {
+  static constexpr int BITS = NT * TK_J < 4096 ? 12 : 32;
+  static constexpr int PER_WORD = 64 / BITS;
+  static constexpr uint64_t MASK = (1ull << BITS) - 1;
+  static_assert((uint64_t)(NT * TK_J) <= MASK && RowShape<NT>::ROUNDS <= 2 * PER_WORD, "fields hold a round's total");
+};
+template <int NT>
 __device__ __forceinline__ void pack_add(Packed &p, int rr, int c) {
-  if (rr < 5)
-    p.w0 += (uint64_t)c << (12 * rr);
+  using PS = PackShape<NT>;
+  if (rr < PS::PER_WORD)
+    p.w0 += (uint64_t)c << (PS::BITS * rr);
   else
-    p.w1 += (uint64_t)c << (12 * (rr - 5));
+    p.w1 += (uint64_t)c << (PS::BITS * (rr - PS::PER_WORD));
 }
+template <int NT>
 __device__ __forceinline__ int pack_get(const Packed &p, int rr) {
-  return (int)((rr < 5 ? p.w0 >> (12 * rr) : p.w1 >> (12 * (rr - 5))) & 0xFFFu);
+  using PS = PackShape<NT>;
+  return (int)((rr < PS::PER_WORD ? p.w0 >> (PS::BITS * rr) : p.w1 >> (PS::BITS * (rr - PS::PER_WORD))) & PS::MASK);
 }
 
 // Exclusive position-order offsets of this thread's per-round counts `cnt`:
 // off[rr] = (items in earlier rounds) + (items of earlier threads in round rr).
 // Returns the block total.
+template <int NT>
 __device__ __forceinline__ int ordered_offsets(const Packed &cnt, uint64_t *sm64, int *off) {
   uint64_t t0, t1;
-  const uint64_t e0 = block_exclusive_scan<TK_THREADS>(cnt.w0, sm64, t0);
-  const uint64_t e1 = block_exclusive_scan<TK_THREADS>(cnt.w1, sm64, t1);
+  const uint64_t e0 = block_exclusive_scan<NT>(cnt.w0, sm64, t0);
+  const uint64_t e1 = block_exclusive_scan<NT>(cnt.w1, sm64, t1);
   const Packed ex{e0, e1}, tot{t0, t1};
   int before = 0;
 #pragma unroll
-  for (int rr = 0; rr < TK_ROUNDS; ++rr) {
-    off[rr] = before + pack_get(ex, rr);
-    before += pack_get(tot, rr);
+  for (int rr = 0; rr < RowShape<NT>::ROUNDS; ++rr) {
+    off[rr] = before + pack_get<NT>(ex, rr);
+    before += pack_get<NT>(tot, rr);
   }
   return before;
 }
@@ -225,11 +248,11 @@ __global__ __launch_bounds__(TK_THREADS) void topk_hist_kernel(const float *__re
   __shared__ uint32_t h[TOPK_BINS];
   zero_lds<TK_THREADS>(h, TOPK_BINS);
   __syncthreads();
-  uint32_t key[TK_PER];
-  load_keys(scores + (int64_t)q * ld, start, n, key);
+  uint32_t key[RowShape<TK_THREADS>::PER];
+  load_keys<TK_THREADS>(scores + (int64_t)q * ld, start, n, key);
   const int t = threadIdx.x;
 #pragma unroll
-  for (int rr = 0; rr < TK_ROUNDS; ++rr)
+  for (int rr = 0; rr < RowShape<TK_THREADS>::ROUNDS; ++rr)
 #pragma unroll
     for (int j = 0; j < TK_J; ++j) atomicAdd(&h[key[TK_J * rr + j] >> 21], 1u);  // padding lands in bin 0
   __syncthreads();
@@ -249,100 +272,85 @@ struct SelectArgs {
   TopkWs ws;
 };
 
-// Three wavefronts per SIMD (at most 168 VGPRs; the 64 keys per thread take
-// 64): left to itself the compiler used 179 and fit two, and with only two rows
-// per CU in flight the row loads, not the selection, set the pace (prefill
-// top-k 0.60 -> 0.43 ms).  Four per SIMD would need spills, which measured
-// slower.
-__global__ __launch_bounds__(TK_THREADS) __attribute__((amdgpu_waves_per_eu(3, 3))) void topk_row_kernel(
-    SelectArgs a) {
-  const int q = blockIdx.x;
-  const int n = a.q_nvis[q];
+// Selects row q (n <= TOPK_ROW_MAX scores) with one block of NT threads:
+// digit 1 from the indexer's histogram or from LDS atomics, digits 2 and 3 as
+// LDS histograms of the keys in the threshold bins, then the position-ordered
+// compaction.  Every thread of the block calls it (it has block barriers).
+template <int NT>
+__device__ void row_select(const SelectArgs &a, const int q, const int n, uint32_t *h, int *sm, uint64_t *sm64,
+                           int *res) {
+  using RS = RowShape<NT>;
   const int k = a.k;
-  __shared__ uint32_t h[TOPK_BINS];
-  __shared__ int sm[TK_THREADS / WAVE];
-  __shared__ uint64_t sm64[TK_THREADS / WAVE];
-  __shared__ int res[2];
   const int t = threadIdx.x;
-  if (n > TOPK_ROW_MAX) {
-    // A long row: only its first-digit threshold bin, once, for the stream
-    // blocks and the finish of this row.
-    const uint32_t *gh = a.ws.hist + (int64_t)q * TOPK_BINS;
-    for (int b = t; b < TOPK_BINS; b += TK_THREADS) h[b] = gh[b];
-    __syncthreads();
-    find_rank_bin<TK_THREADS, TOPK_BINS>(h, k, sm, res);
-    if (t == 0) a.ws.b1info[q] = make_uint2((uint32_t)res[0], (uint32_t)res[1]);
-    return;
-  }
   int32_t *out = a.idx + (int64_t)q * k;
   if (n <= k) {
-    write_short(out, a.count, q, n, k, TK_THREADS);
+    write_short(out, a.count, q, n, k, NT);
     return;
   }
-  uint32_t key[TK_PER];
-  load_keys(a.scores + (int64_t)q * a.ld, 0, n, key);
+  uint32_t key[RS::PER];
+  load_keys<NT>(a.scores + (int64_t)q * a.ld, 0, (int)min((int64_t)n, a.ld), key);  // never past the row's ld
   // Digit 1: key[31:21].
   if (a.hist1_valid) {
     const uint32_t *gh = a.ws.hist + (int64_t)q * TOPK_BINS;
-    for (int b = t; b < TOPK_BINS; b += TK_THREADS) h[b] = gh[b];
+    for (int b = t; b < TOPK_BINS; b += NT) h[b] = gh[b];
   } else {
-    zero_lds<TK_THREADS>(h, TOPK_BINS);
+    zero_lds<NT>(h, TOPK_BINS);
     __syncthreads();
 #pragma unroll
-    for (int rr = 0; rr < TK_ROUNDS; ++rr)
+    for (int rr = 0; rr < RS::ROUNDS; ++rr)
 #pragma unroll
       for (int j = 0; j < TK_J; ++j)
         atomicAdd(&h[key[TK_J * rr + j] >> 21], 1u);  // padding keys land in bin 0
   }
   __syncthreads();
-  find_rank_bin<TK_THREADS, TOPK_BINS>(h, k, sm, res);
+  find_rank_bin<NT, TOPK_BINS>(h, k, sm, res);
   const uint32_t b1 = (uint32_t)res[0];
   const int r = k - res[1];
   __syncthreads();
   // Digit 2: key[20:10] of the keys in bin B1.
-  zero_lds<TK_THREADS>(h, TOPK_BINS);
+  zero_lds<NT>(h, TOPK_BINS);
   __syncthreads();
 #pragma unroll
-  for (int rr = 0; rr < TK_ROUNDS; ++rr)
+  for (int rr = 0; rr < RS::ROUNDS; ++rr)
 #pragma unroll
     for (int j = 0; j < TK_J; ++j) {
       const uint32_t kk = key[TK_J * rr + j];
       if ((kk >> 21) == b1) atomicAdd(&h[(kk >> 10) & 2047u], 1u);
     }
   __syncthreads();
-  find_rank_bin<TK_THREADS, TOPK_BINS>(h, r, sm, res);
+  find_rank_bin<NT, TOPK_BINS>(h, r, sm, res);
   const uint32_t pre = (b1 << 11) | (uint32_t)res[0];
   const int r2 = r - res[1];
   __syncthreads();
   // Digit 3: key[9:0] of the keys with key[31:10] == pre.
-  zero_lds<TK_THREADS>(h, 1024);
+  zero_lds<NT>(h, 1024);
   __syncthreads();
 #pragma unroll
-  for (int rr = 0; rr < TK_ROUNDS; ++rr)
+  for (int rr = 0; rr < RS::ROUNDS; ++rr)
 #pragma unroll
     for (int j = 0; j < TK_J; ++j) {
       const uint32_t kk = key[TK_J * rr + j];
       if ((kk >> 10) == pre) atomicAdd(&h[kk & 1023u], 1u);
     }
   __syncthreads();
-  find_rank_bin<TK_THREADS, 1024>(h, r2, sm, res);
+  find_rank_bin<NT, 1024>(h, r2, sm, res);
   const uint32_t kth = (pre << 10) | (uint32_t)res[0];
   const int ties = r2 - res[1];
   // Emit in position order: keys > kth, and the first `ties` keys == kth.
   Packed tc{0, 0};
 #pragma unroll
-  for (int rr = 0; rr < TK_ROUNDS; ++rr) {
+  for (int rr = 0; rr < RS::ROUNDS; ++rr) {
     int c = 0;
 #pragma unroll
     for (int j = 0; j < TK_J; ++j) c += (key[TK_J * rr + j] == kth) ? 1 : 0;
-    pack_add(tc, rr, c);
+    pack_add<NT>(tc, rr, c);
   }
-  int toff[TK_ROUNDS];
-  ordered_offsets(tc, sm64, toff);
+  int toff[RS::ROUNDS];
+  ordered_offsets<NT>(tc, sm64, toff);
   Packed sc{0, 0};
-  uint32_t selbits[TK_ROUNDS];
+  uint32_t selbits[RS::ROUNDS];
 #pragma unroll
-  for (int rr = 0; rr < TK_ROUNDS; ++rr) {
+  for (int rr = 0; rr < RS::ROUNDS; ++rr) {
     int tr = toff[rr], c = 0;
     uint32_t bits = 0;
 #pragma unroll
@@ -355,23 +363,38 @@ __global__ __launch_bounds__(TK_THREADS) __attribute__((amdgpu_waves_per_eu(3, 3
       bits |= (uint32_t)sel << j;
     }
     selbits[rr] = bits;
-    pack_add(sc, rr, c);
+    pack_add<NT>(sc, rr, c);
   }
-  int soff[TK_ROUNDS];
-  const int tot = ordered_offsets(sc, sm64, soff);
+  int soff[RS::ROUNDS];
+  const int tot = ordered_offsets<NT>(sc, sm64, soff);
 #pragma unroll
-  for (int rr = 0; rr < TK_ROUNDS; ++rr) {
+  for (int rr = 0; rr < RS::ROUNDS; ++rr) {
     int pos = soff[rr];
 #pragma unroll
     for (int j = 0; j < TK_J; ++j)
       if (selbits[rr] & (1u << j)) {
-        if (pos < k) out[pos] = slot_pos(t, rr, j);
+        if (pos < k) out[pos] = slot_pos<NT>(t, rr, j);
         ++pos;
       }
   }
-  for (int i = tot + t; i < k; i += TK_THREADS) out[i] = -1;  // defensive: tot == k
+  for (int i = tot + t; i < k; i += NT) out[i] = -1;  // defensive: tot == k
   if (t == 0 && a.count) a.count[q] = min(tot, k);
 }
+
+// Three wavefronts per SIMD (at most 168 VGPRs; the 64 keys per thread take
+// 64): left to itself the compiler used 179 and fit two, and with only two rows
+// per CU in flight the row loads, not the selection, set the pace (prefill
+// top-k 0.60 -> 0.43 ms).  Four per SIMD would need spills, which measured
+// slower.  Launched only when every row fits TOPK_ROW_MAX.
+__global__ __launch_bounds__(TK_THREADS) __attribute__((amdgpu_waves_per_eu(3, 3))) void topk_row_kernel(
+    SelectArgs a) {
+  __shared__ uint32_t h[TOPK_BINS];
+  __shared__ int sm[TK_THREADS / WAVE];
+  __shared__ uint64_t sm64[TK_THREADS / WAVE];
+  __shared__ int res[2];
+  row_select<TK_THREADS>(a, blockIdx.x, a.q_nvis[blockIdx.x], h, sm, sm64, res);
+}
+
 
 // Lanes below this one in the wavefront (mbcnt over a ballot mask).
 __device__ __forceinline__ int lanes_below(uint64_t m) {
@@ -397,7 +420,14 @@ __global__ __launch_bounds__(LONG_THREADS) void topk_long_kernel(SelectArgs a) {
   const int c = blockIdx.x - q * nblk;
   const int n = a.q_nvis[q];
   const int k = a.k;
-  if (n <= TOPK_ROW_MAX) return;  // topk_row_kernel
+  __shared__ uint32_t h[TOPK_BINS];
+  __shared__ int sm[LONG_THREADS / WAVE];
+  __shared__ uint64_t sm64[LONG_THREADS / WAVE];
+  __shared__ int res[2];
+  if (n <= TOPK_ROW_MAX) {  // a short row of a batch with long rows: its first block selects it
+    if (c == 0) row_select<LONG_THREADS>(a, q, n, h, sm, sm64, res);
+    return;
+  }
   const int nb = (n + TOPK_LONG_SPAN - 1) / TOPK_LONG_SPAN;
   if (c >= nb) return;
   const int t = threadIdx.x;
@@ -405,6 +435,13 @@ __global__ __launch_bounds__(LONG_THREADS) void topk_long_kernel(SelectArgs a) {
   const int p0 = c * TOPK_LONG_SPAN + wave * TOPK_WAVE_SPAN;
   const int p1 = min(n, p0 + TOPK_WAVE_SPAN);
   const float *row = a.scores + (int64_t)q * a.ld;
+
+  // The row's first-digit histogram is requested before the scores: loads
+  // complete in issue order, so the wait for it does not wait for them.
+  const uint32_t *gh = a.ws.hist + (int64_t)q * TOPK_BINS;
+  uint32_t hv[TOPK_BINS / LONG_THREADS];
+#pragma unroll
+  for (int i = 0; i < TOPK_BINS / LONG_THREADS; ++i) hv[i] = gh[t + i * LONG_THREADS];
 
   // All score loads first.  Lane l reads positions p0 + 512 u + 8 l .. +7 of
   // round u; a float4 at a position < p1 stays inside the row (ld % 4 == 0),
@@ -418,7 +455,14 @@ __global__ __launch_bounds__(LONG_THREADS) void topk_long_kernel(SelectArgs a) {
       f[u][hh] = *reinterpret_cast<const float4 *>(row + (ii < p1 ? ii : 0));
     }
 
-  const uint32_t b1 = a.ws.b1info[q].x;  // threshold bin B1 (row kernel)
+  // Threshold bin B1 of the first digit and the count above it, computed by
+  // every block of the row alike; the first block publishes it for the finish.
+#pragma unroll
+  for (int i = 0; i < TOPK_BINS / LONG_THREADS; ++i) h[t + i * LONG_THREADS] = hv[i];
+  __syncthreads();
+  find_rank_bin<LONG_THREADS, TOPK_BINS>(h, k, sm, res);
+  const uint32_t b1 = (uint32_t)res[0];
+  if (c == 0 && t == 0) a.ws.b1info[q] = make_uint2((uint32_t)res[0], (uint32_t)res[1]);
 
   // Candidates in position order.
   uint2 *lst = a.ws.cand + (((int64_t)q * nblk + c) * TOPK_LONG_WAVES + wave) * TOPK_WAVE_SPAN;
@@ -597,12 +641,16 @@ hipError_t launch_topk_select(const float *scores, int64_t ld, const int32_t *q_
                               hipStream_t st) {
   if (num_q == 0) return hipSuccess;
   SelectArgs a{scores, ld, q_nvis, k, hist1_valid ? 1 : 0, idx, count, ws};
-  hipLaunchKernelGGL(topk_row_kernel, dim3((unsigned)num_q), dim3(TK_THREADS), 0, st, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || ws.nblk == 0 || max_nvis <= TOPK_ROW_MAX) return e;
+  if (ws.nblk == 0 || max_nvis <= TOPK_ROW_MAX) {  // every row fits one row block
+    hipLaunchKernelGGL(topk_row_kernel, dim3((unsigned)num_q), dim3(TK_THREADS), 0, st, a);
+    return hipGetLastError();
+  }
+  // Some row is long: the long kernel finds each long row's threshold bin and
+  // candidates, and selects each short row with its first block; the finish
+  // kernel completes the long rows.
   const int64_t blocks = (int64_t)num_q * ws.nblk;
   hipLaunchKernelGGL(topk_long_kernel, dim3((unsigned)blocks), dim3(LONG_THREADS), 0, st, a);
-  e = hipGetLastError();
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(topk_finish_kernel, dim3((unsigned)num_q), dim3(LONG_THREADS), 0, st, a);
   return hipGetLastError();
