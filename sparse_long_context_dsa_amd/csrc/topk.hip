@@ -14,30 +14,33 @@
 // is a position-ordered compaction built from block-wide exclusive scans, so
 // it is deterministic.
 //
-// A block of 256 threads owns 16384 consecutive scores, 64 per thread in
-// registers: in each of 8 rounds every thread reads 8 consecutive scores and
-// consecutive lanes read consecutive 32-byte pieces, so each load instruction
-// covers whole cache lines.  Position order is (round, thread, element); the
-// per-round counts of a thread are packed into two 64-bit words (12 bits per
-// round) so that one pair of scans orders all 8 rounds.
+// A row block owns up to 16384 consecutive scores in registers: 256 threads
+// with 64 each (8 rounds), or 1024 threads with 16 each (2 rounds).  In each
+// round every thread reads 8 consecutive scores and consecutive lanes read
+// consecutive 32-byte pieces, so each load instruction covers whole cache
+// lines.  Position order is (round, thread, element); the per-round counts of
+// a thread are packed into two 64-bit words so that one pair of scans orders
+// all rounds.
 //
-// Kernels, chosen per query by its history length n:
-//  * topk_row_kernel (n <= 16384, e.g. every causal-prefill row): one block
-//    per query; only the histograms live in LDS, so many rows are selected per
-//    CU at once.  The first-digit histogram comes from the indexer's fused
-//    epilogue when available, else from LDS atomics.
-//  * longer rows (e.g. 128K decode): the row kernel's block of such a row
-//    finds the threshold bin B1 of the first digit (and the count above it)
-//    from the histogram built with the scores; topk_long_kernel blocks of 16
+// Kernels, chosen per batch by its longest history:
+//  * every row n <= 16384 (e.g. causal prefill): topk_row_kernel, one
+//    256-thread block per query; only the histograms live in LDS, so several
+//    rows are selected per CU at once.  The first-digit histogram comes from
+//    the indexer's fused epilogue when available, else from LDS atomics.
+//  * some row longer (e.g. 128K decode): topk_long_kernel blocks of 16
 //    wavefronts, each owning 32768 consecutive positions (2048 per
-//    wavefront), stream the scores once and append the candidates (digit >=
-//    B1, about k + |B1| per row) to per-wavefront lists in position order,
-//    ranks from ballots; topk_finish_kernel (one block per long row, after
-//    the kernel boundary has published the lists) loads the lists into LDS in
-//    position order and finishes there: digits 2 and 3 as LDS histograms of
-//    the candidates, then the output as a position-ordered compaction.  (Handing the row to its last block inside
-//    one kernel would need an agent-scope fence per block, which on this
-//    part writes back and invalidates the XCD's L2 and costs far more.)
+//    wavefront), first find the row's threshold bin B1 of the first digit
+//    (and the count above it) from the histogram built with the scores, then
+//    stream the scores once and append the candidates (digit >= B1, about
+//    k + |B1| per row) to per-wavefront lists in position order, ranks from
+//    ballots.  A short row of such a batch is selected whole by its first
+//    1024-thread block, as a row block.  topk_finish_kernel (one block per
+//    long row, after the kernel boundary has published the lists) loads the
+//    lists into LDS in position order and finishes there: digits 2 and 3 as
+//    LDS histograms of the candidates, then the output as a position-ordered
+//    compaction.  (Handing the row to its last block inside one kernel would
+//    need an agent-scope fence per block, which on this part writes back and
+//    invalidates the XCD's L2 and costs far more.)
 #include "device_util.h"
 #include "dsa_internal.h"
 
