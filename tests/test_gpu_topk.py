@@ -113,3 +113,18 @@ def test_long_row_boundaries():
             rng.standard_normal(1 << 20).astype(np.float32),
             np.full(1 << 20, 0.25, np.float32)]
     assert_same(rows, nvis, 2048, "long boundaries")
+
+
+def test_short_rows_beside_long_rows():
+    """A batch with one long row sends its short rows through the long-row
+    kernel's 1024-thread row selection: the largest short row (16384), one
+    just above k, exactly k, a tiny one, with coarse values (many ties at the
+    threshold), next to a long row."""
+    banner("topk short rows beside a long row")
+    rng = np.random.default_rng(23)
+    nvis = [16384, 2049, 2048, 5, 40000]
+    rows = [np.round(rng.standard_normal(n) * 3).astype(np.float32) for n in nvis]
+    rows[0][::7] = 0.0
+    rows[0][3::11] = -0.0
+    assert_same(rows, nvis, 2048, "short beside long")
+    assert_same(rows, nvis, 7, "short beside long, k = 7")
