@@ -14,25 +14,28 @@
 // c_s = g_s * k_scale_s and e_j = w[t,j] * q_scale[t,j].
 //
 // One block (4 wavefronts) = one query and a run of up to 2048 members of its
-// set, in tiles of 64 keys:
+// set (1024 in the dense mode), in tiles of 64 keys:
 //   * D on FP8 MFMA (v_mfma_scale_f32_16x16x128_f8f6f4), as in the forward
 //     indexer: wavefront w scores keys 16w .. 16w+15 of the tile against all 64
 //     heads, the keys loaded straight into B-operand registers (the next tile's
 //     one tile ahead);
-//   * the 0/1 gates [D > 0] go to LDS as a [key][head] and a [head][key] bf16
-//     matrix, and c_s k8_s as a [dim][key] pair of bf16 matrices hi + lo
-//     (hi = bf16(x), lo = bf16(x - hi); hi + lo is within 2^-17 |x| of x), so that
-//     both contractions run on bf16 MFMA (v_mfma_f32_32x32x16_bf16) with
-//     products exact in fp32;
+//   * the 0/1 gates [D > 0] go to LDS as a [key][head] bf16 matrix, and
+//     c_s k8_s as a [key][dim] pair of bf16 matrices hi + lo (hi = bf16(x),
+//     lo = bf16(x - hi); hi + lo is within 2^-17 |x| of x), so that both
+//     contractions run on bf16 MFMA (v_mfma_f32_32x32x16_bf16) with products
+//     exact in fp32.  Each lane writes whole 8- and 16-byte pieces of its key's
+//     row;
 //   * dkh of the tile = gates[key][head] . (e q8)[head][dim], whose B operand
 //     (hi + lo) stays in registers for the whole block, then times g_s into dk
 //     by fp32 atomic adds (a key row may belong to several queries);
-//   * dqh += gates[head][key] . (c k8)[key][dim] accumulates in registers over
-//     the block's tiles; dw accumulates in-lane from D.
+//   * dqh += gates^T[head][key] . (c k8)[key][dim] accumulates in registers
+//     over the block's tiles, both operands read key-major through the
+//     transposing LDS read ds_read_b64_tr_b16; dw accumulates in-lane from D.
 // Wavefront w owns the 32 x 64 quarter (rows 32 (w & 1), columns 64 (w >> 1))
-// of both 64 x 128 products.  Rows of the LDS matrices are padded to 144
-// bytes, so the 16-byte fragment reads of 32 consecutive rows spread over the
-// banks.
+// of both 64 x 128 products.  The 16-byte chunks of each LDS row are XOR-
+// swizzled by the row so that the writes, the 16-byte reads of 16 consecutive
+// rows and the transposing reads of 4 rows x 64 bytes all spread over the 64
+// banks without conflicts.
 #include "device_util.h"
 #include "dsa_internal.h"
 
@@ -41,13 +44,24 @@ namespace dsa {
 constexpr int IB_THREADS = 256;
 constexpr int IB_TILE = 64;                 // keys per tile
 constexpr int IB_MAX_MEMBERS = 2048;        // members per block
-constexpr int IB_PER_THREAD = IB_MAX_MEMBERS / IB_THREADS;
 constexpr int IB_MIN_BLOCKS = 1024;
-constexpr int IB_LD = 72;                   // bf16 per padded LDS row (144 bytes)
 constexpr uint32_t IB_INVALID = 0x80000000u;
 constexpr uint16_t BF16_ONE = 0x3F80;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+
+// Byte offset of byte b of row r in the [key][head] gate matrix (128-byte
+// rows) and in the [key][dim] c k8 matrices (256-byte rows): the 16-byte chunk
+// index is XORed with a function of the row's low four bits.
+__device__ __forceinline__ int gate_off(int r, int b) {
+  const int sw = (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  return r * 128 + (((b >> 4) ^ sw) << 4) + (b & 15);
+}
+__device__ __forceinline__ int ck_off(int r, int b) {
+  const int sw = ((r & 3) << 2) | ((r >> 2) & 3);
+  return r * 256 + (((b >> 4) ^ sw) << 4) + (b & 15);
+}
 
 struct IndexerBwdArgs {
   IndexerBwdLaunch a;
@@ -94,13 +108,16 @@ __global__ __launch_bounds__(IB_THREADS) void indexer_bwd_kernel(IndexerBwdArgs 
   const int l31 = lane & 31, g2 = lane >> 5;    // bf16 32x32 MFMA lane split
   const int half = wave & 1, dn0 = 2 * (wave >> 1);
 
-  __shared__ __attribute__((aligned(16))) uint16_t gk[IB_TILE * IB_LD];    // [key][head] gates
-  __shared__ __attribute__((aligned(16))) uint16_t gh[64 * IB_LD];         // [head][key] gates
-  __shared__ __attribute__((aligned(16))) uint16_t chi[128 * IB_LD];       // [dim][key] c k8, hi
-  __shared__ __attribute__((aligned(16))) uint16_t clo[128 * IB_LD];       // [dim][key] c k8, lo
-  __shared__ uint32_t mrow[IB_MAX_MEMBERS];  // physical row (IB_INVALID: not a member)
-  __shared__ float mg[IB_MAX_MEMBERS];       // g_s (0 for non-members)
-  __shared__ float mc[IB_MAX_MEMBERS];       // c_s = g_s * k_scale_s
+  __shared__ __attribute__((aligned(16))) uint8_t gts[IB_TILE * 128];  // [key][head] gates, bf16
+  __shared__ __attribute__((aligned(16))) uint8_t chs[IB_TILE * 256];  // [key][dim] c k8, hi
+  __shared__ __attribute__((aligned(16))) uint8_t cls[IB_TILE * 256];  // [key][dim] c k8, lo
+  // The dense instantiation (no dk) keeps no g_s and half the members, so
+  // that three workgroups fit a CU's LDS.
+  constexpr int MAXM = DK ? IB_MAX_MEMBERS : IB_MAX_MEMBERS / 2;
+  constexpr int PER = MAXM / IB_THREADS;
+  __shared__ uint32_t mrow[MAXM];     // physical row (IB_INVALID: not a member)
+  __shared__ float mg[DK ? MAXM : 1];  // g_s (0 for non-members)
+  __shared__ float mc[MAXM];          // c_s = g_s * k_scale_s
   __shared__ float dwred[4][64];
 
   // Members -> rows, g and c, all loads issued before any is used.  A
@@ -109,34 +126,34 @@ __global__ __launch_bounds__(IB_THREADS) void indexer_bwd_kernel(IndexerBwdArgs 
   const int seq = a.q_seq[t];
   const int ntile = (nmem + IB_TILE - 1) / IB_TILE;
   {
-    int pos[IB_PER_THREAD];
-    float gv[IB_PER_THREAD];
+    int pos[PER];
+    float gv[PER];
     const int lastm = nmem - 1;
 #pragma unroll
-    for (int j = 0; j < IB_PER_THREAD; ++j) {
+    for (int j = 0; j < PER; ++j) {
       const int i = min(tid + j * IB_THREADS, lastm);
       pos[j] = a.idx ? a.idx[(int64_t)t * a.k + m0 + i] : m0 + i;
     }
 #pragma unroll
-    for (int j = 0; j < IB_PER_THREAD; ++j) {
+    for (int j = 0; j < PER; ++j) {
       const int i = min(tid + j * IB_THREADS, lastm);
       const bool ok = pos[j] >= 0 && pos[j] < nvis;
       gv[j] = a.grad[(int64_t)t * a.ld_grad + (a.idx ? m0 + i : (ok ? pos[j] : 0))];
       pos[j] = ok ? pos[j] : -1;
     }
-    uint32_t row[IB_PER_THREAD];
+    uint32_t row[PER];
 #pragma unroll
-    for (int j = 0; j < IB_PER_THREAD; ++j) row[j] = (uint32_t)phys_row(a.map, seq, max(pos[j], 0));
-    float ks[IB_PER_THREAD];
+    for (int j = 0; j < PER; ++j) row[j] = (uint32_t)phys_row(a.map, seq, max(pos[j], 0));
+    float ks[PER];
 #pragma unroll
-    for (int j = 0; j < IB_PER_THREAD; ++j) ks[j] = a.k_scale[row[j]];
+    for (int j = 0; j < PER; ++j) ks[j] = a.k_scale[row[j]];
 #pragma unroll
-    for (int j = 0; j < IB_PER_THREAD; ++j) {
+    for (int j = 0; j < PER; ++j) {
       const int i = tid + j * IB_THREADS;
       if (i < ntile * IB_TILE) {
         const bool ok = i < nmem && pos[j] >= 0;
         mrow[i] = row[j] | (ok ? 0u : IB_INVALID);
-        mg[i] = ok ? gv[j] : 0.0f;
+        if (DK) mg[i] = ok ? gv[j] : 0.0f;
         mc[i] = ok ? gv[j] * ks[j] : 0.0f;
       }
     }
@@ -173,6 +190,34 @@ __global__ __launch_bounds__(IB_THREADS) void indexer_bwd_kernel(IndexerBwdArgs 
     }
   __syncthreads();  // member table ready
 
+  // Byte offsets into the tile matrices.  Writes: the gates of heads
+  // 16 mt + 4 g4 .. + 3 of key kl (8 bytes), c k8 of dims 32 g4 + 8 j .. + 7
+  // of key kl (16 bytes).  Transposing reads (dq's A from the gates, its B
+  // from c k8): lane 32 g2 + 16 th + ti points at row ti >> 2 of the key set
+  // 16 ks + 8 g2 + 4 hh .. + 3 and bytes 8 (ti & 3) of its group's 32-byte
+  // column span, and receives column 16 th + ti of those 4 keys.  The
+  // swizzles do not depend on ks, so ks moves the offsets by whole rows.
+  const int kl = 16 * wave + l15;  // this lane's key within a tile
+  const int ti = lane & 15, th = (lane >> 4) & 1;
+  int gw_off[4], cw_off[4], ga_off[2], cb_off[2][2];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) gw_off[mt] = gate_off(kl, 32 * mt + 8 * g4);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) cw_off[j] = ck_off(kl, 64 * g4 + 16 * j);
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const int r = 8 * g2 + 4 * hh + (ti >> 2);
+    ga_off[hh] = gate_off(r, 64 * half + 32 * th + 8 * (ti & 3));
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) cb_off[hh][nt] = ck_off(r, 64 * (dn0 + nt) + 32 * th + 8 * (ti & 3));
+  }
+  auto tr_pair = [](const uint8_t *p0, const uint8_t *p1) {
+    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)p0);
+    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)p1);
+    const uint2 ulo = __builtin_bit_cast(uint2, lo), uhi = __builtin_bit_cast(uint2, hi);
+    return make_uint4(ulo.x, ulo.y, uhi.x, uhi.y);
+  };
+
   v16f dq[2];
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt)
@@ -204,32 +249,34 @@ __global__ __launch_bounds__(IB_THREADS) void indexer_bwd_kernel(IndexerBwdArgs 
       for (int i = 0; i < 4; ++i) dwa[mt][i] = fmaf(fmaxf(d[mt][i], 0.0f), ck, dwa[mt][i]);
 
     __syncthreads();  // the previous tile's fragment reads are done
-    const int kl = 16 * wave + l15;  // key within the tile
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       uint16_t gt[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) gt[i] = d[mt][i] > 0.0f ? BF16_ONE : (uint16_t)0;
-      if (DK)
-        *reinterpret_cast<uint2 *>(&gk[kl * IB_LD + 16 * mt + 4 * g4]) =
-            make_uint2(gt[0] | (uint32_t)gt[1] << 16, gt[2] | (uint32_t)gt[3] << 16);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) gh[(16 * mt + 4 * g4 + i) * IB_LD + kl] = gt[i];
+      *reinterpret_cast<uint2 *>(gts + gw_off[mt]) =
+          make_uint2(gt[0] | (uint32_t)gt[1] << 16, gt[2] | (uint32_t)gt[3] << 16);
     }
+    // c k8 of this lane's key, dims 32 g4 + 8 j .. + 7 (key words 2 j, 2 j + 1).
     const uint32_t kw[8] = {(uint32_t)kb[0], (uint32_t)kb[1], (uint32_t)kb[2], (uint32_t)kb[3],
                             (uint32_t)kb[4], (uint32_t)kb[5], (uint32_t)kb[6], (uint32_t)kb[7]};
 #pragma unroll
-    for (int wd = 0; wd < 8; ++wd) {
-      float kv[4];
-      fp8x4(kw[wd], kv);
+    for (int j = 0; j < 4; ++j) {
+      uint32_t hw[4], lw[4];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const float x = ck * kv[b];
-        const uint16_t hi = bf16_bits(x);
-        const int o = (32 * g4 + 4 * wd + b) * IB_LD + kl;
-        chi[o] = hi;
-        clo[o] = bf16_bits(x - bf16_value(hi));
+      for (int h2 = 0; h2 < 2; ++h2) {
+        float kv[4];
+        fp8x4(kw[2 * j + h2], kv);
+#pragma unroll
+        for (int b = 0; b < 4; b += 2) {
+          const float x0 = ck * kv[b], x1 = ck * kv[b + 1];
+          const uint16_t h0 = bf16_bits(x0), h1 = bf16_bits(x1);
+          hw[2 * h2 + b / 2] = h0 | (uint32_t)h1 << 16;
+          lw[2 * h2 + b / 2] = bf16_bits(x0 - bf16_value(h0)) | (uint32_t)bf16_bits(x1 - bf16_value(h1)) << 16;
+        }
       }
+      *reinterpret_cast<uint4 *>(chs + cw_off[j]) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      *reinterpret_cast<uint4 *>(cls + cw_off[j]) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
     }
     __syncthreads();  // gates and c k8 visible
 
@@ -242,7 +289,7 @@ __global__ __launch_bounds__(IB_THREADS) void indexer_bwd_kernel(IndexerBwdArgs 
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       if (!DK) break;
-      const uint4 ga = *reinterpret_cast<const uint4 *>(&gk[(32 * half + l31) * IB_LD + 16 * ks + 8 * g2]);
+      const uint4 ga = *reinterpret_cast<const uint4 *>(gts + gate_off(32 * half + l31, 32 * ks + 16 * g2));
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         dk[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(ga), as_bf8(bkh[nt][ks]), dk[nt], 0, 0, 0);
@@ -252,12 +299,11 @@ __global__ __launch_bounds__(IB_THREADS) void indexer_bwd_kernel(IndexerBwdArgs 
     // dqh of heads 32 half .. + 31, dims 32 (dn0 + nt) + l31, over the tile's 64 keys.
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const uint4 ga = *reinterpret_cast<const uint4 *>(&gh[(32 * half + l31) * IB_LD + 16 * ks + 8 * g2]);
+      const uint4 ga = tr_pair(gts + ga_off[0] + 2048 * ks, gts + ga_off[1] + 2048 * ks);
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
-        const int o = (32 * (dn0 + nt) + l31) * IB_LD + 16 * ks + 8 * g2;
-        const uint4 bh = *reinterpret_cast<const uint4 *>(&chi[o]);
-        const uint4 bl = *reinterpret_cast<const uint4 *>(&clo[o]);
+        const uint4 bh = tr_pair(chs + cb_off[0][nt] + 4096 * ks, chs + cb_off[1][nt] + 4096 * ks);
+        const uint4 bl = tr_pair(cls + cb_off[0][nt] + 4096 * ks, cls + cb_off[1][nt] + 4096 * ks);
         dq[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(ga), as_bf8(bh), dq[nt], 0, 0, 0);
         dq[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(ga), as_bf8(bl), dq[nt], 0, 0, 0);
       }
@@ -323,9 +369,12 @@ __global__ __launch_bounds__(IB_THREADS) void indexer_bwd_kernel(IndexerBwdArgs 
 //   * D^T = K . Q^T on FP8 MFMA: the tile's keys are the A operand for the
 //     whole block (all 64 keys in every wavefront), wavefront w takes heads
 //     16w .. 16w+15 of the query as the B operand;
-//   * a[key][head] = [D > 0] e_j g_s goes to LDS as bf16 hi + lo and q8 as a
-//     [dim][head] bf16 matrix, and dkh += a . q8 runs on bf16 MFMA with the
-//     same 32 x 64 quarters per wavefront as the query-major kernel.
+//   * a[key][head] = [D > 0] e_j g_s goes to LDS head-major, as bf16 hi + lo
+//     (each lane writes 4 adjacent keys of its head at once), and q8 as a
+//     [head][dim] bf16 matrix (16-byte writes); dkh += a . q8 runs on bf16 MFMA
+//     with the same 32 x 64 quarters per wavefront as the query-major kernel,
+//     both operands read through the transposing LDS read, with the same
+//     swizzles as there.
 // Query order within a block is the index order (a block-wide scan), so a
 // block's sum is deterministic; blocks of the same tile meet in the atomic adds.
 constexpr int IBK_QRUN = 512;  // query indices per block
@@ -353,9 +402,9 @@ __global__ __launch_bounds__(IB_THREADS) void indexer_bwd_dk_kernel(IndexerBwdDk
   // Two sets, alternating between queries: query i writes set i & 1 while
   // slower wavefronts may still read set (i - 1) & 1, so one barrier per
   // query suffices.
-  __shared__ __attribute__((aligned(16))) uint16_t ahi[2][IB_TILE * IB_LD];  // [key][head]
-  __shared__ __attribute__((aligned(16))) uint16_t alo[2][IB_TILE * IB_LD];
-  __shared__ __attribute__((aligned(16))) uint16_t qt[2][128 * IB_LD];       // [dim][head]
+  __shared__ __attribute__((aligned(16))) uint8_t ahi[2][64 * 128];  // [head][key], gate_off
+  __shared__ __attribute__((aligned(16))) uint8_t alo[2][64 * 128];
+  __shared__ __attribute__((aligned(16))) uint8_t qt[2][64 * 256];   // [head][dim], ck_off
   __shared__ int qlist[IBK_QRUN];
   __shared__ int sm[IB_THREADS / WAVE];
   __shared__ int lsh[IB_THREADS / WAVE];
@@ -432,43 +481,72 @@ __global__ __launch_bounds__(IB_THREADS) void indexer_bwd_dk_kernel(IndexerBwdDk
       }
   };
 
+  // LDS byte offsets.  Writes: head j = 16 wave + l15, dims 32 g4 + 8 jj ..
+  // + 7 of q8 (16 bytes) and keys 16 mt + 4 g4 .. + 3 of a (8 bytes).
+  // Transposing reads (heads are the k index of the product): lane
+  // 32 g2 + 16 th + ti points at row (head) ti >> 2 of the set
+  // 16 ks + 8 g2 + 4 hh .. + 3 and bytes 8 (ti & 3) of its group's 32-byte
+  // column span, and receives column 16 th + ti: key 32 half + l31 of a, or
+  // dim 32 (dn0 + nt) + l31 of q8.
+  const int ti = lane & 15, th = (lane >> 4) & 1;
+  int qw_off[4], aw_off[4], ar_off[2], qr_off[2][2];
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) qw_off[jj] = ck_off(16 * wave + l15, 64 * g4 + 16 * jj);
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) aw_off[mt] = gate_off(16 * wave + l15, 32 * mt + 8 * g4);
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const int r = 8 * g2 + 4 * hh + (ti >> 2);
+    ar_off[hh] = gate_off(r, 64 * half + 32 * th + 8 * (ti & 3));
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) qr_off[hh][nt] = ck_off(r, 64 * (dn0 + nt) + 32 * th + 8 * (ti & 3));
+  }
+  auto tr_pair = [](const uint8_t *p0, const uint8_t *p1) {
+    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)p0);
+    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)p1);
+    const uint2 ulo = __builtin_bit_cast(uint2, lo), uhi = __builtin_bit_cast(uint2, hi);
+    return make_uint4(ulo.x, ulo.y, uhi.x, uhi.y);
+  };
+
   auto one_query = [&](const QueryOps &o, const int set) {
-    const int j = 16 * wave + l15;
-    uint16_t *qts = qt[set];
-    uint16_t *ah = ahi[set];
-    uint16_t *al = alo[set];
-    // q8 of head j as bf16, transposed: qt[dim][head].
+    uint8_t *qts = qt[set];
+    uint8_t *ah = ahi[set];
+    uint8_t *al = alo[set];
+    // q8 of head j as bf16: qt[head][dim], dims 32 g4 + 8 jj .. + 7 (words 2 jj, 2 jj + 1).
     const uint32_t qw[8] = {(uint32_t)o.qb[0], (uint32_t)o.qb[1], (uint32_t)o.qb[2], (uint32_t)o.qb[3],
                             (uint32_t)o.qb[4], (uint32_t)o.qb[5], (uint32_t)o.qb[6], (uint32_t)o.qb[7]};
 #pragma unroll
-    for (int wd = 0; wd < 8; ++wd) {
-      float qv[4];
-      fp8x4(qw[wd], qv);
+    for (int jj = 0; jj < 4; ++jj) {
+      float qv[8];
+      fp8x4(qw[2 * jj], qv);
+      fp8x4(qw[2 * jj + 1], qv + 4);
+      uint32_t u[4];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) qts[(32 * g4 + 4 * wd + b) * IB_LD + j] = bf16_bits(qv[b]);
+      for (int b = 0; b < 4; ++b) u[b] = bf16_bits(qv[2 * b]) | (uint32_t)bf16_bits(qv[2 * b + 1]) << 16;
+      *reinterpret_cast<uint4 *>(qts + qw_off[jj]) = make_uint4(u[0], u[1], u[2], u[3]);
     }
     // D^T[key][head] for keys 16 mt + 4 g4 + i, head j; a = [D > 0] e_j g_s.
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       const v4f d = mfma_fp8_16x16x128(ka[mt], o.qb, v4f{0.f, 0.f, 0.f, 0.f});
+      uint16_t hi[4], lo[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int key = 16 * mt + 4 * g4 + i;
         const float x = d[i] > 0.0f ? o.e * o.g[4 * mt + i] : 0.0f;
-        const uint16_t hi = bf16_bits(x);
-        ah[key * IB_LD + j] = hi;
-        al[key * IB_LD + j] = bf16_bits(x - bf16_value(hi));
+        hi[i] = bf16_bits(x);
+        lo[i] = bf16_bits(x - bf16_value(hi[i]));
       }
+      *reinterpret_cast<uint2 *>(ah + aw_off[mt]) = make_uint2(hi[0] | (uint32_t)hi[1] << 16, hi[2] | (uint32_t)hi[3] << 16);
+      *reinterpret_cast<uint2 *>(al + aw_off[mt]) = make_uint2(lo[0] | (uint32_t)lo[1] << 16, lo[2] | (uint32_t)lo[3] << 16);
     }
-    __syncthreads();  // this query's a and q8^T visible
+    __syncthreads();  // this query's a and q8 visible
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const int ao = (32 * half + l31) * IB_LD + 16 * ks + 8 * g2;
-      const uint4 fh = *reinterpret_cast<const uint4 *>(&ah[ao]);
-      const uint4 fl = *reinterpret_cast<const uint4 *>(&al[ao]);
+      const uint4 fh = tr_pair(ah + ar_off[0] + 2048 * ks, ah + ar_off[1] + 2048 * ks);
+      const uint4 fl = tr_pair(al + ar_off[0] + 2048 * ks, al + ar_off[1] + 2048 * ks);
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
-        const uint4 b = *reinterpret_cast<const uint4 *>(&qts[(32 * (dn0 + nt) + l31) * IB_LD + 16 * ks + 8 * g2]);
+        const uint4 b = tr_pair(qts + qr_off[0][nt] + 4096 * ks, qts + qr_off[1][nt] + 4096 * ks);
         acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(fh), as_bf8(b), acc[nt], 0, 0, 0);
         acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(fl), as_bf8(b), acc[nt], 0, 0, 0);
       }
@@ -507,7 +585,7 @@ hipError_t launch_indexer_bwd(const IndexerBwdLaunch &a, int max_set, hipStream_
   if (e != hipSuccess || max_set == 0) return e;
   IndexerBwdArgs p;
   p.a = a;
-  int members = IB_MAX_MEMBERS;
+  int members = a.idx ? IB_MAX_MEMBERS : IB_MAX_MEMBERS / 2;  // the kernel's MAXM
   auto chunks = [&](int m) { return (max_set + m - 1) / m; };
   while (members > IB_TILE && (int64_t)a.num_q * chunks(members) < IB_MIN_BLOCKS) members /= 2;
   p.members = members;
