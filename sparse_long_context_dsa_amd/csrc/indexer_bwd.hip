@@ -14,23 +14,25 @@
 // c_s = g_s * k_scale_s and e_j = w[t,j] * q_scale[t,j].
 //
 // One block (4 wavefronts) = one query and a run of up to 2048 members of its
-// set (1024 in the dense mode), in tiles of 64 keys:
+// set, in tiles of 64 keys:
 //   * D on FP8 MFMA (v_mfma_scale_f32_16x16x128_f8f6f4), as in the forward
 //     indexer: wavefront w scores keys 16w .. 16w+15 of the tile against all 64
 //     heads, the keys loaded straight into B-operand registers (the next tile's
 //     one tile ahead);
-//   * the 0/1 gates [D > 0] go to LDS as a [key][head] bf16 matrix, and
-//     c_s k8_s as a [key][dim] pair of bf16 matrices hi + lo (hi = bf16(x),
-//     lo = bf16(x - hi); hi + lo is within 2^-17 |x| of x), so that both
-//     contractions run on bf16 MFMA (v_mfma_f32_32x32x16_bf16) with products
-//     exact in fp32.  Each lane writes whole 8- and 16-byte pieces of its key's
-//     row;
+//   * the gates [D > 0] go to LDS as [key][head] bf16 matrices: times c_s,
+//     split into bf16 hi + lo (hi = bf16(c), lo = bf16(c - hi); hi + lo is
+//     within 2^-17 |c| of c), for dq, and as plain 0/1 for dk; the keys go
+//     as a [key][dim] bf16 matrix (FP8 E4M3 values are exact in bf16).  Both
+//     contractions then run on bf16 MFMA (v_mfma_f32_32x32x16_bf16) with
+//     products exact in fp32.  Each lane writes whole 8- and 16-byte pieces
+//     of its key's rows;
 //   * dkh of the tile = gates[key][head] . (e q8)[head][dim], whose B operand
 //     (hi + lo) stays in registers for the whole block, then times g_s into dk
 //     by fp32 atomic adds (a key row may belong to several queries);
-//   * dqh += gates^T[head][key] . (c k8)[key][dim] accumulates in registers
-//     over the block's tiles, both operands read key-major through the
-//     transposing LDS read ds_read_b64_tr_b16; dw accumulates in-lane from D.
+//   * dqh += (gates c)^T[head][key] . k8[key][dim] (hi and lo) accumulates in
+//     registers over the block's tiles, both operands read key-major through
+//     the transposing LDS read ds_read_b64_tr_b16; dw accumulates in-lane
+//     from D.
 // Wavefront w owns the 32 x 64 quarter (rows 32 (w & 1), columns 64 (w >> 1))
 // of both 64 x 128 products.  The 16-byte chunks of each LDS row are XOR-
 // swizzled by the row so that the writes, the 16-byte reads of 16 consecutive
@@ -49,6 +51,8 @@ constexpr uint32_t IB_INVALID = 0x80000000u;
 constexpr uint16_t BF16_ONE = 0x3F80;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
 typedef short v4s __attribute__((ext_vector_type(4)));
 
 // Byte offset of byte b of row r in the [key][head] gate matrix (128-byte
@@ -73,6 +77,10 @@ __device__ __forceinline__ uint16_t bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, (__bf16)x);  // round to nearest even
 }
 __device__ __forceinline__ float bf16_value(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+// Two fp32 values as a bf16 pair (round to nearest even), the first in the low half.
+__device__ __forceinline__ uint32_t pk_bf16(float2_t v) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
 __device__ __forceinline__ bf16x8_t as_bf8(const uint4 &u) { return __builtin_bit_cast(bf16x8_t, u); }
 // The four FP8 E4M3 bytes of word v as fp32 (exact), lowest byte first.
 __device__ __forceinline__ void fp8x4(uint32_t v, float *f) {
@@ -87,8 +95,10 @@ __global__ __launch_bounds__(256) void ib_zero_kernel(float *__restrict__ p, int
   if (i < n) p[i] = 0.0f;
 }
 
+// The dense instantiation is held to three workgroups per CU (its LDS allows
+// three; uncapped, the compiler's register use would allow two).
 template <bool DK>
-__global__ __launch_bounds__(IB_THREADS) void indexer_bwd_kernel(IndexerBwdArgs p) {
+__global__ __launch_bounds__(IB_THREADS, DK ? 1 : 3) void indexer_bwd_kernel(IndexerBwdArgs p) {
   const IndexerBwdLaunch &a = p.a;
   const int t = blockIdx.x / p.nchunk;
   const int chunk = blockIdx.x - t * p.nchunk;
@@ -108,16 +118,16 @@ __global__ __launch_bounds__(IB_THREADS) void indexer_bwd_kernel(IndexerBwdArgs 
   const int l31 = lane & 31, g2 = lane >> 5;    // bf16 32x32 MFMA lane split
   const int half = wave & 1, dn0 = 2 * (wave >> 1);
 
-  __shared__ __attribute__((aligned(16))) uint8_t gts[IB_TILE * 128];  // [key][head] gates, bf16
-  __shared__ __attribute__((aligned(16))) uint8_t chs[IB_TILE * 256];  // [key][dim] c k8, hi
-  __shared__ __attribute__((aligned(16))) uint8_t cls[IB_TILE * 256];  // [key][dim] c k8, lo
-  // The dense instantiation (no dk) keeps no g_s and half the members, so
-  // that three workgroups fit a CU's LDS.
-  constexpr int MAXM = DK ? IB_MAX_MEMBERS : IB_MAX_MEMBERS / 2;
-  constexpr int PER = MAXM / IB_THREADS;
-  __shared__ uint32_t mrow[MAXM];     // physical row (IB_INVALID: not a member)
-  __shared__ float mg[DK ? MAXM : 1];  // g_s (0 for non-members)
-  __shared__ float mc[MAXM];          // c_s = g_s * k_scale_s
+  __shared__ __attribute__((aligned(16))) uint8_t gts[DK ? IB_TILE * 128 : 16];  // [key][head] gates (dk)
+  __shared__ __attribute__((aligned(16))) uint8_t ghs[IB_TILE * 128];  // [key][head] gates x c_s, hi
+  __shared__ __attribute__((aligned(16))) uint8_t gls[IB_TILE * 128];  // [key][head] gates x c_s, lo
+  __shared__ __attribute__((aligned(16))) uint8_t kbs[IB_TILE * 256];  // [key][dim] k8 as bf16
+  // The dense instantiation (no dk) keeps no g_s and no plain gates, so that
+  // three workgroups fit a CU's LDS.
+  constexpr int PER = IB_MAX_MEMBERS / IB_THREADS;
+  __shared__ uint32_t mrow[IB_MAX_MEMBERS];           // physical row (IB_INVALID: not a member)
+  __shared__ float mg[DK ? IB_MAX_MEMBERS : 1];       // g_s (0 for non-members)
+  __shared__ float mc[IB_MAX_MEMBERS];                // c_s = g_s * k_scale_s
   __shared__ float dwred[4][64];
 
   // Members -> rows, g and c, all loads issued before any is used.  A
@@ -248,37 +258,39 @@ __global__ __launch_bounds__(IB_THREADS) void indexer_bwd_kernel(IndexerBwdArgs 
 #pragma unroll
       for (int i = 0; i < 4; ++i) dwa[mt][i] = fmaf(fmaxf(d[mt][i], 0.0f), ck, dwa[mt][i]);
 
+    // c_s as bf16 hi + lo (c - hi is exact in fp32); hi + lo is within
+    // 2^-17 |c| of c.
+    const uint32_t chb = bf16_bits(ck);
+    const uint32_t clb = bf16_bits(ck - bf16_value((uint16_t)chb));
     __syncthreads();  // the previous tile's fragment reads are done
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      uint16_t gt[4];
+      bool on[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) gt[i] = d[mt][i] > 0.0f ? BF16_ONE : (uint16_t)0;
-      *reinterpret_cast<uint2 *>(gts + gw_off[mt]) =
-          make_uint2(gt[0] | (uint32_t)gt[1] << 16, gt[2] | (uint32_t)gt[3] << 16);
+      for (int i = 0; i < 4; ++i) on[i] = d[mt][i] > 0.0f;
+      if (DK)
+        *reinterpret_cast<uint2 *>(gts + gw_off[mt]) =
+            make_uint2((on[0] ? BF16_ONE : 0u) | (on[1] ? (uint32_t)BF16_ONE << 16 : 0u),
+                       (on[2] ? BF16_ONE : 0u) | (on[3] ? (uint32_t)BF16_ONE << 16 : 0u));
+      *reinterpret_cast<uint2 *>(ghs + gw_off[mt]) =
+          make_uint2((on[0] ? chb : 0u) | (on[1] ? chb << 16 : 0u), (on[2] ? chb : 0u) | (on[3] ? chb << 16 : 0u));
+      *reinterpret_cast<uint2 *>(gls + gw_off[mt]) =
+          make_uint2((on[0] ? clb : 0u) | (on[1] ? clb << 16 : 0u), (on[2] ? clb : 0u) | (on[3] ? clb << 16 : 0u));
     }
-    // c k8 of this lane's key, dims 32 g4 + 8 j .. + 7 (key words 2 j, 2 j + 1).
-    const uint32_t kw[8] = {(uint32_t)kb[0], (uint32_t)kb[1], (uint32_t)kb[2], (uint32_t)kb[3],
-                            (uint32_t)kb[4], (uint32_t)kb[5], (uint32_t)kb[6], (uint32_t)kb[7]};
+    // k8 of this lane's key as bf16 (exact), dims 32 g4 + 8 j .. + 7 (key
+    // words 2 j, 2 j + 1).
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      uint32_t hw[4], lw[4];
+      uint32_t u[4];
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
-        float kv[4];
-        fp8x4(kw[2 * j + h2], kv);
-#pragma unroll
-        for (int b = 0; b < 4; b += 2) {
-          const float x0 = ck * kv[b], x1 = ck * kv[b + 1];
-          const uint16_t h0 = bf16_bits(x0), h1 = bf16_bits(x1);
-          hw[2 * h2 + b / 2] = h0 | (uint32_t)h1 << 16;
-          lw[2 * h2 + b / 2] = bf16_bits(x0 - bf16_value(h0)) | (uint32_t)bf16_bits(x1 - bf16_value(h1)) << 16;
-        }
+        const int v = kb[2 * j + h2];
+        u[2 * h2] = pk_bf16(__builtin_amdgcn_cvt_pk_f32_fp8(v, false));
+        u[2 * h2 + 1] = pk_bf16(__builtin_amdgcn_cvt_pk_f32_fp8(v, true));
       }
-      *reinterpret_cast<uint4 *>(chs + cw_off[j]) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-      *reinterpret_cast<uint4 *>(cls + cw_off[j]) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+      *reinterpret_cast<uint4 *>(kbs + cw_off[j]) = make_uint4(u[0], u[1], u[2], u[3]);
     }
-    __syncthreads();  // gates and c k8 visible
+    __syncthreads();  // gates and k8 visible
 
     // dkh of the tile's keys 32 half .. + 31, dims 32 (dn0 + nt) + l31.
     v16f dk[2];
@@ -299,13 +311,13 @@ __global__ __launch_bounds__(IB_THREADS) void indexer_bwd_kernel(IndexerBwdArgs 
     // dqh of heads 32 half .. + 31, dims 32 (dn0 + nt) + l31, over the tile's 64 keys.
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const uint4 ga = tr_pair(gts + ga_off[0] + 2048 * ks, gts + ga_off[1] + 2048 * ks);
+      const uint4 ah = tr_pair(ghs + ga_off[0] + 2048 * ks, ghs + ga_off[1] + 2048 * ks);
+      const uint4 al = tr_pair(gls + ga_off[0] + 2048 * ks, gls + ga_off[1] + 2048 * ks);
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
-        const uint4 bh = tr_pair(chs + cb_off[0][nt] + 4096 * ks, chs + cb_off[1][nt] + 4096 * ks);
-        const uint4 bl = tr_pair(cls + cb_off[0][nt] + 4096 * ks, cls + cb_off[1][nt] + 4096 * ks);
-        dq[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(ga), as_bf8(bh), dq[nt], 0, 0, 0);
-        dq[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(ga), as_bf8(bl), dq[nt], 0, 0, 0);
+        const uint4 b = tr_pair(kbs + cb_off[0][nt] + 4096 * ks, kbs + cb_off[1][nt] + 4096 * ks);
+        dq[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(ah), as_bf8(b), dq[nt], 0, 0, 0);
+        dq[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf8(al), as_bf8(b), dq[nt], 0, 0, 0);
       }
     }
     // dk rows: accumulator register r holds key 8 (r >> 2) + 4 g2 + (r & 3).
@@ -464,21 +476,36 @@ __global__ __launch_bounds__(IB_THREADS) void indexer_bwd_dk_kernel(IndexerBwdDk
     float e;
     float g[16];
   };
+  // Offsets from the query's (uniform) bases are 32-bit byte counts, so the
+  // loads take a scalar base and a 32-bit lane offset.
+  auto at = [](const auto *base, uint32_t byte_off) {
+    return reinterpret_cast<decltype(base)>(reinterpret_cast<const char *>(base) + byte_off);
+  };
   auto load_q = [&](int i, QueryOps &o) {
-    const int t = qlist[min(i, n_rel - 1)];
+    const int t = __builtin_amdgcn_readfirstlane(qlist[min(i, n_rel - 1)]);
     const int j = 16 * wave + l15;
-    o.qb = load32(a.q8 + (int64_t)t * (64 * 128) + j * 128 + 32 * g4);
-    const float qs = a.q_scale ? a.q_scale[(int64_t)t * 64 + j] : 1.0f;
-    o.e = a.w[(int64_t)t * 64 + j] * qs;
+    o.qb = load32(at(a.q8 + (int64_t)t * (64 * 128), (uint32_t)(j * 128 + 32 * g4)));
+    const float qs = a.q_scale ? *at(a.q_scale + (int64_t)t * 64, 4u * j) : 1.0f;
+    o.e = *at(a.w + (int64_t)t * 64, 4u * j) * qs;
     const int nv = a.q_nvis[t];
     const float *gr = a.grad + (int64_t)t * a.ld_grad;
+    if (nv >= s0 + IB_TILE) {  // uniform: the whole tile is in the history
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int i2 = 0; i2 < 4; ++i2) {
-        const int pos = s0 + 16 * mt + 4 * g4 + i2;
-        o.g[4 * mt + i2] = pos < nv ? gr[pos] : 0.0f;
-      }
+        for (int i2 = 0; i2 < 4; ++i2) o.g[4 * mt + i2] = *at(gr, 4u * (uint32_t)(s0 + 16 * mt + 4 * g4 + i2));
+    } else {
+      // The run holds only queries with n_vis > s0, so n_vis - 1 is a valid
+      // position to read in place of those past the history.
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i2 = 0; i2 < 4; ++i2) {
+          const int pos = s0 + 16 * mt + 4 * g4 + i2;
+          const float gv = *at(gr, 4u * (uint32_t)min(pos, nv - 1));
+          o.g[4 * mt + i2] = pos < nv ? gv : 0.0f;
+        }
+    }
   };
 
   // LDS byte offsets.  Writes: head j = 16 wave + l15, dims 32 g4 + 8 jj ..
@@ -517,27 +544,31 @@ __global__ __launch_bounds__(IB_THREADS) void indexer_bwd_dk_kernel(IndexerBwdDk
                             (uint32_t)o.qb[4], (uint32_t)o.qb[5], (uint32_t)o.qb[6], (uint32_t)o.qb[7]};
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      float qv[8];
-      fp8x4(qw[2 * jj], qv);
-      fp8x4(qw[2 * jj + 1], qv + 4);
       uint32_t u[4];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) u[b] = bf16_bits(qv[2 * b]) | (uint32_t)bf16_bits(qv[2 * b + 1]) << 16;
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int v = (int)qw[2 * jj + h2];
+        u[2 * h2] = pk_bf16(__builtin_amdgcn_cvt_pk_f32_fp8(v, false));
+        u[2 * h2 + 1] = pk_bf16(__builtin_amdgcn_cvt_pk_f32_fp8(v, true));
+      }
       *reinterpret_cast<uint4 *>(qts + qw_off[jj]) = make_uint4(u[0], u[1], u[2], u[3]);
     }
     // D^T[key][head] for keys 16 mt + 4 g4 + i, head j; a = [D > 0] e_j g_s.
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       const v4f d = mfma_fp8_16x16x128(ka[mt], o.qb, v4f{0.f, 0.f, 0.f, 0.f});
-      uint16_t hi[4], lo[4];
+      float x[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float x = d[i] > 0.0f ? o.e * o.g[4 * mt + i] : 0.0f;
-        hi[i] = bf16_bits(x);
-        lo[i] = bf16_bits(x - bf16_value(hi[i]));
+      for (int i = 0; i < 4; ++i) x[i] = d[i] > 0.0f ? o.e * o.g[4 * mt + i] : 0.0f;
+      uint32_t hi[2], lo[2];
+#pragma unroll
+      for (int p2 = 0; p2 < 2; ++p2) {
+        hi[p2] = pk_bf16(float2_t{x[2 * p2], x[2 * p2 + 1]});
+        lo[p2] = pk_bf16(float2_t{x[2 * p2] - __uint_as_float(hi[p2] << 16),
+                                  x[2 * p2 + 1] - __uint_as_float(hi[p2] & 0xFFFF0000u)});
       }
-      *reinterpret_cast<uint2 *>(ah + aw_off[mt]) = make_uint2(hi[0] | (uint32_t)hi[1] << 16, hi[2] | (uint32_t)hi[3] << 16);
-      *reinterpret_cast<uint2 *>(al + aw_off[mt]) = make_uint2(lo[0] | (uint32_t)lo[1] << 16, lo[2] | (uint32_t)lo[3] << 16);
+      *reinterpret_cast<uint2 *>(ah + aw_off[mt]) = make_uint2(hi[0], hi[1]);
+      *reinterpret_cast<uint2 *>(al + aw_off[mt]) = make_uint2(lo[0], lo[1]);
     }
     __syncthreads();  // this query's a and q8 visible
 #pragma unroll
@@ -585,7 +616,7 @@ hipError_t launch_indexer_bwd(const IndexerBwdLaunch &a, int max_set, hipStream_
   if (e != hipSuccess || max_set == 0) return e;
   IndexerBwdArgs p;
   p.a = a;
-  int members = a.idx ? IB_MAX_MEMBERS : IB_MAX_MEMBERS / 2;  // the kernel's MAXM
+  int members = IB_MAX_MEMBERS;
   auto chunks = [&](int m) { return (max_set + m - 1) / m; };
   while (members > IB_TILE && (int64_t)a.num_q * chunks(members) < IB_MIN_BLOCKS) members /= 2;
   p.members = members;
