@@ -502,7 +502,7 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(decode shards by sequence with no exchange; see the design notes). "
               f"Got --gpus {args.gpus}, WORLD_SIZE {world}.", file=sys.stderr)
         sys.exit(2)

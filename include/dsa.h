@@ -65,7 +65,7 @@ enum {
 typedef enum dsa_status {
   DSA_OK = 0,
   DSA_ERR_INVALID_ARG = 1, /* null pointer, bad size, k out of [1, 2048], misalignment */
-  DSA_ERR_UNSUPPORTED = 2, /* a shape or layout this build does not handle */
+  DSA_ERR_UNSUPPORTED = 2, /* a shape or layout this library does not handle */
   DSA_ERR_WORKSPACE = 3,   /* ws is NULL or smaller than dsa_workspace_bytes() */
   DSA_ERR_HIP = 4          /* a HIP launch failed */
 } dsa_status;
