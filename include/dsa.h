@@ -267,8 +267,7 @@ int dsa_indexer_kl_dense(const dsa_queries *queries, const dsa_kv_layout *layout
  *   dk     : fp32 [R, 128], ADDED to (zero it first): a key row collects the
  *            terms of every query whose set holds it.
  * dk is summed with fp32 atomics, and so are dq and dw when a query's set is
- * split over workgroups (sets of more than 2048 members, 1024 when idx =
- * NULL, or small batches):
+ * split over workgroups (sets of more than 2048 members, or small batches):
  * there the rounding order, and so the last bits, can differ between runs.
  * With one query per key row and one workgroup per query the result is
  * deterministic.  No workspace. */
