@@ -204,6 +204,14 @@ int dsa_sparse_mla_decode(const dsa_queries *queries, const dsa_kv_layout *layou
 int dsa_dense_mla(const dsa_queries *queries, const dsa_kv_layout *layout, const uint16_t *q,
                   const uint16_t *kv, float softmax_scale, float *out, float *lse, void *ws,
                   size_t ws_bytes, hipStream_t stream);
+/* Sparse attention for many queries per call (causal prefill: query t of a
+ * sequence attends to its selected positions among s < t; page "arXiv'25 |
+ * DSA ...", section 3, third equation; page "DeepSeekV3.2之DSA", part 5.1).
+ * The same function as dsa_sparse_mla_decode, scheduled with one workgroup
+ * per query (no row splits, no partial results): the matrix-core pipeline
+ * overlaps each tile's gather, QK^T, softmax and PV.  Arguments as for
+ * dsa_sparse_mla_decode; ws may be NULL (dsa_workspace_bytes(
+ * DSA_OP_MLA_PREFILL, ...) is 0). */
 int dsa_sparse_mla_prefill(const dsa_queries *queries, const dsa_kv_layout *layout,
                            const uint16_t *q, const uint16_t *kv, const int32_t *idx,
                            const int32_t *count, int32_t k, float softmax_scale,
@@ -224,7 +232,10 @@ int dsa_sparse_mla_prefill(const dsa_queries *queries, const dsa_kv_layout *layo
  *           q, kv and lse; a head whose lse is not finite contributes 0);
  *   scores : fp32 [num_q, ld_scores], the indexer's I by position; it must hold
  *           every position of the set (the short-history bypass of dsa_forward
- *           does not score, so training calls dsa_indexer_scores for all);
+ *           does not score, so training calls dsa_indexer_scores for all).  A
+ *           score may be -inf (softmax weight 0: its gradient is -p, and its KL
+ *           term is +inf where p > 0) but not NaN or +inf, and a non-empty set
+ *           needs at least one finite score;
  *   grad   : fp32 [num_q, k] dL/dI in set order (entry j belongs to idx[i, j];
  *           0 past count and for entries not in the set);
  *   target : fp32 [num_q, k] p in the same order, or NULL;

@@ -42,17 +42,33 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _on_device(t):
+    return t.is_cuda
+
+
 def _need(t, dtype, shape=None, name="tensor"):
+    """dtype, then shape, then device and layout: a host tensor of the wrong
+    shape is reported as a shape error."""
     if t is None:
         raise ValueError(f"{name} is required")
     if t.dtype != dtype:
         raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
-    if not t.is_cuda:
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not _on_device(t):
         raise ValueError(f"{name} must be a device tensor")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
-    if shape is not None and tuple(t.shape) != tuple(shape):
-        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def _need_rows(t, dtype, rows, name, min_cols=0):
+    """A 2-D [rows, ld] tensor with ld >= min_cols (row-major, ld = its width):
+    the kernels index row i at i * ld, so fewer rows would be read or written
+    past the allocation."""
+    _need(t, dtype, None, name)
+    if t.dim() != 2 or t.shape[0] != rows or t.shape[1] < min_cols:
+        raise ValueError(f"{name}: expected shape ({rows}, ld) with ld >= {min_cols}, got {tuple(t.shape)}")
     return t
 
 
@@ -92,6 +108,8 @@ class KvLayout:
             _need(self.seq_row0, torch.int64, (self.num_seqs,), "seq_row0")
             return KvLayoutC(self.num_seqs, 0, 0, 0, self.num_rows, None, self.seq_row0.data_ptr())
         bt = _need(self.block_table, torch.int32, None, "block_table")
+        if bt.dim() != 2 or bt.shape[0] != self.num_seqs or bt.shape[1] < 1:
+            raise ValueError(f"block_table: expected shape ({self.num_seqs}, max_blocks), got {tuple(bt.shape)}")
         return KvLayoutC(self.num_seqs, self.block_size, int(bt.shape[1]), 0, self.num_rows, bt.data_ptr(), None)
 
 
@@ -136,7 +154,7 @@ def dsa_indexer_scores_e8m0(queries: Queries, layout: KvLayout, q_fp8, q_scale, 
     _need(w, torch.float32, (nq, DSA_HI), "w")
     _need(k_fp8, torch.uint8, (layout.num_rows, DSA_DI), "k_fp8")
     _need(k_scale_e8m0, torch.uint8, (layout.num_rows,), "k_scale_e8m0")
-    _need(scores, torch.float32, None, "scores")
+    _need_rows(scores, torch.float32, nq, "scores", queries.max_nvis)
     qc, lc = queries.c(), layout.c()
     _lib.check("dsa_indexer_scores_e8m0", _lib.lib().dsa_indexer_scores_e8m0(
         ctypes.byref(qc), ctypes.byref(lc), _ptr(q_fp8), _ptr(q_scale), _ptr(w), _ptr(k_fp8),
@@ -152,7 +170,7 @@ def dsa_indexer_scores(queries: Queries, layout: KvLayout, q_fp8, q_scale, w, k_
     _need(w, torch.float32, (nq, DSA_HI), "w")
     _need(k_fp8, torch.uint8, (layout.num_rows, DSA_DI), "k_fp8")
     _need(k_scale, torch.float32, (layout.num_rows,), "k_scale")
-    _need(scores, torch.float32, None, "scores")
+    _need_rows(scores, torch.float32, nq, "scores", queries.max_nvis)
     qc, lc = queries.c(), layout.c()
     _lib.check("dsa_indexer_scores", _lib.lib().dsa_indexer_scores(
         ctypes.byref(qc), ctypes.byref(lc), _ptr(q_fp8), _ptr(q_scale), _ptr(w), _ptr(k_fp8),
@@ -165,7 +183,7 @@ def dsa_topk(queries: Queries, scores, k: int, idx, count=None, ws=None, stream=
     if count is not None:
         _need(count, torch.int32, (nq,), "count")
     if scores is not None:
-        _need(scores, torch.float32, None, "scores")
+        _need_rows(scores, torch.float32, nq, "scores", queries.max_nvis)
     if ws is None:
         ws = workspace(DSA_OP_TOPK, queries, k, idx.device)
     qc = queries.c()
@@ -234,7 +252,7 @@ def dsa_indexer_kl_sparse(queries, layout, q, kv, idx, count, k, lse, softmax_sc
     if count is not None:
         _need(count, torch.int32, (nq,), "count")
     _need(lse, torch.float32, (nq, DSA_H), "lse")
-    _need(scores, torch.float32, None, "scores")
+    _need_rows(scores, torch.float32, nq, "scores", queries.max_nvis)
     _need(grad, torch.float32, (nq, k), "grad")
     _need(kl, torch.float32, (nq,), "kl")
     if target is not None:
@@ -256,8 +274,8 @@ def dsa_indexer_kl_dense(queries, layout, q, kv, lse, softmax_scale, scores, gra
     _need(q, torch.bfloat16, (nq, DSA_H, DSA_D), "q")
     _need(kv, torch.bfloat16, (layout.num_rows, DSA_D), "kv")
     _need(lse, torch.float32, (nq, DSA_H), "lse")
-    _need(scores, torch.float32, None, "scores")
-    _need(grad, torch.float32, None, "grad")
+    _need_rows(scores, torch.float32, nq, "scores", queries.max_nvis)
+    _need_rows(grad, torch.float32, nq, "grad", queries.max_nvis)
     _need(kl, torch.float32, (nq,), "kl")
     if target is not None:
         _need(target, torch.float32, tuple(grad.shape), "target")
@@ -287,7 +305,7 @@ def dsa_indexer_backward(queries, layout, q_fp8, q_scale, w, k_fp8, k_scale, idx
         _need(idx, torch.int32, (nq, k), "idx")
         _need(grad, torch.float32, (nq, k), "grad")
     else:
-        _need(grad, torch.float32, None, "grad")
+        _need_rows(grad, torch.float32, nq, "grad", queries.max_nvis)
         k = 0
     if count is not None:
         _need(count, torch.int32, (nq,), "count")

@@ -292,6 +292,7 @@ __global__ __launch_bounds__(KL_THREADS) void kl_loss_kernel(KlLaunch a) {
     if (pos < 0 || pos >= nvis) continue;
     sa += gr[i];
     const float x = sc[pos];
+    if (x == -INFINITY) continue;  // softmax weight 0 (and exp(-inf - -inf) would be NaN)
     if (x > m) {
       se = se * expf(m - x) + 1.0f;
       m = x;

@@ -163,3 +163,76 @@ def test_kl_and_backward_accept_empty_batches():
                                   None, 0, None, None, None, None) == 0
     assert L.dsa_indexer_kl_dense(ctypes.byref(q), ctypes.byref(lay), None, None, None, 0.07, None, 0, None, None, 0,
                                   None, None, None) == 0
+
+
+# --------------------------------------------------------------------------- #
+# The Python binding's own checks: row counts of the [num_q, ld] arrays and of
+# the block table.  The C layer only sees ld, so a tensor with fewer rows than
+# num_q would be indexed past its end on the device; the binding must refuse it
+# before any call.  Host tensors stand in for device tensors here (the device
+# test is patched out), and every case fails a check before the library is
+# called.
+# --------------------------------------------------------------------------- #
+@pytest.fixture
+def host_as_device(monkeypatch):
+    import torch
+    monkeypatch.setattr(dsa, "_on_device", lambda t: True)
+    return torch
+
+
+def _host_inputs(torch, nq=3, nvis=100, rows=500):
+    q = dsa.Queries(torch.zeros(nq, dtype=torch.int32), torch.full((nq,), nvis, dtype=torch.int32), nvis)
+    lay = dsa.KvLayout(1, rows, seq_row0=torch.zeros(1, dtype=torch.int64))
+    t = dict(
+        q8=torch.zeros((nq, 64, 128), dtype=torch.uint8), qs=torch.ones((nq, 64)), w=torch.ones((nq, 64)),
+        k8=torch.zeros((rows, 128), dtype=torch.uint8), ks=torch.ones(rows),
+        ke=torch.zeros(rows, dtype=torch.uint8), qm=torch.zeros((nq, 128, 576), dtype=torch.bfloat16),
+        kv=torch.zeros((rows, 576), dtype=torch.bfloat16), lse=torch.zeros((nq, 128)), kl=torch.zeros(nq),
+        idx=torch.zeros((nq, 2048), dtype=torch.int32), dq=torch.zeros((nq, 64, 128)), dw=torch.zeros((nq, 64)),
+        dk=torch.zeros((rows, 128)))
+    return q, lay, t
+
+
+def test_binding_rejects_score_rows_short_of_num_q(host_as_device):
+    torch = host_as_device
+    q, lay, t = _host_inputs(torch)
+    short = torch.zeros((2, 128))  # 3 queries
+    narrow = torch.zeros((3, 64))  # max_nvis = 100
+    for scores, what in ((short, "scores"), (narrow, "scores"), (torch.zeros(3 * 128), "scores")):
+        with pytest.raises(ValueError, match=what):
+            dsa.dsa_indexer_scores(q, lay, t["q8"], t["qs"], t["w"], t["k8"], t["ks"], scores)
+        with pytest.raises(ValueError, match=what):
+            dsa.dsa_indexer_scores_e8m0(q, lay, t["q8"], t["qs"], t["w"], t["k8"], t["ke"], scores)
+        with pytest.raises(ValueError, match=what):
+            dsa.dsa_topk(q, scores, 2048, t["idx"], ws=torch.zeros(1, dtype=torch.uint8))
+        with pytest.raises(ValueError, match=what):
+            dsa.dsa_indexer_kl_sparse(q, lay, t["qm"], t["kv"], t["idx"], None, 2048, t["lse"], 0.07, scores,
+                                      torch.zeros((3, 2048)), t["kl"])
+        with pytest.raises(ValueError, match=what):
+            dsa.dsa_indexer_kl_dense(q, lay, t["qm"], t["kv"], t["lse"], 0.07, scores, torch.zeros((3, 128)),
+                                     t["kl"])
+
+
+def test_binding_rejects_grad_rows_short_of_num_q(host_as_device):
+    torch = host_as_device
+    q, lay, t = _host_inputs(torch)
+    scores = torch.zeros((3, 128))
+    for grad in (torch.zeros((2, 128)), torch.zeros((3, 99)), torch.zeros(384)):
+        with pytest.raises(ValueError, match="grad"):
+            dsa.dsa_indexer_kl_dense(q, lay, t["qm"], t["kv"], t["lse"], 0.07, scores, grad, t["kl"])
+        with pytest.raises(ValueError, match="grad"):
+            dsa.dsa_indexer_backward(q, lay, t["q8"], t["qs"], t["w"], t["k8"], t["ks"], None, None, 0, grad,
+                                     t["dq"], t["dw"], t["dk"])
+    with pytest.raises(ValueError, match="target"):
+        dsa.dsa_indexer_kl_dense(q, lay, t["qm"], t["kv"], t["lse"], 0.07, scores, torch.zeros((3, 128)), t["kl"],
+                                 target=torch.zeros((2, 128)))
+
+
+def test_binding_rejects_block_table_rows_short_of_num_seqs(host_as_device):
+    torch = host_as_device
+    for bt in (torch.zeros((1, 4), dtype=torch.int32), torch.zeros(8, dtype=torch.int32),
+               torch.zeros((2, 0), dtype=torch.int32)):
+        lay = dsa.KvLayout(2, 256, block_table=bt, block_size=64)
+        with pytest.raises(ValueError, match="block_table"):
+            lay.c()
+    dsa.KvLayout(2, 256, block_table=torch.zeros((2, 4), dtype=torch.int32), block_size=64).c()

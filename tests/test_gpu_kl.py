@@ -246,3 +246,31 @@ def test_kl_degenerate_cases():
                              e.view(0, 64), e, loss=loss_t)
     torch.cuda.synchronize()
     assert loss_t.item() == 0.0
+
+
+def test_kl_minus_inf_scores():
+    """Indexer scores of -inf (softmax weight 0), including each query's first
+    set member: no NaN; the gradient is -p there and Softmax - p elsewhere, and
+    the KL term is +inf (the target puts mass on every member)."""
+    banner("kl -inf scores")
+    wl = make_custom(seq_lens=[300, 2500], device="cuda", seed=69)
+    k = 2048
+    idx, cnt = random_selection(wl, k, 18)
+    s_h, _ = synthetic_scores(wl, 19)
+    for i in range(wl.nq):
+        s_h[i, idx[i, :cnt[i]:7]] = -np.inf  # every 7th member, member 0 included
+    grad, target, kl, loss, _ = run_sparse(wl, idx, cnt, k, torch.from_numpy(s_h).cuda())
+    ov = OracleView(wl)
+    for i in range(wl.nq):
+        c = int(cnt[i])
+        pos = idx[i, :c]
+        r = ov.rows(i, pos)
+        kv = bf16_bits(wl.kv[torch.from_numpy(r).cuda()])
+        kl_ref, g_ref, p_ref, _ = oracle.indexer_kl_query(bf16_bits(wl.q_mla[i]), kv, s_h[i, pos].astype(np.float64),
+                                                          wl.softmax_scale)
+        assert kl_ref == np.inf and kl[i] == np.inf, f"q{i}: kl {kl[i]}"
+        assert np.isfinite(grad[i, :c]).all() and np.isfinite(target[i, :c]).all()
+        assert (np.abs(target[i, :c] - p_ref) <= P_RTOL * p_ref + 1e-12).all()
+        soft = g_ref + p_ref
+        assert (np.abs(grad[i, :c] - g_ref) <= P_RTOL * (p_ref + soft) + 1e-12).all(), f"q{i}: grad"
+    assert loss == np.inf

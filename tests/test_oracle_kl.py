@@ -217,3 +217,27 @@ def test_backward_inactive_relu_gives_zero():
     kh = -np.abs(rng.standard_normal((7, 8)))  # every dot negative
     dw, dq, dk = kl.indexer_backward_query(qh, rng.standard_normal(5), kh, rng.standard_normal(7))
     assert not dw.any() and not dq.any() and not dk.any()
+
+
+def test_kl_with_minus_inf_logits():
+    """A logit of -inf has softmax weight 0.  Where p is 0 too the entry drops
+    out: KL and the other gradients equal scipy's over the finite entries, and
+    its own gradient is 0.  Where p > 0 the KL is +inf and the gradient -p."""
+    rng = np.random.default_rng(21)
+    n = 40
+    x = rng.standard_normal(n) * 2.0
+    dead = np.zeros(n, bool)
+    dead[[0, 7, 19, 39]] = True
+    x[dead] = -np.inf
+    p = rng.dirichlet(np.ones(n))
+    p[dead] = 0.0
+    p /= p.sum()
+    got, grad, _ = kl.kl_to_softmax(p, x)
+    live = ~dead
+    assert got == pytest.approx(sp.rel_entr(p[live], sp.softmax(x[live])).sum(), rel=1e-12)
+    assert np.allclose(grad[live], sp.softmax(x[live]) - p[live], rtol=0, atol=1e-15)
+    assert (grad[dead] == 0.0).all()
+    p2 = rng.dirichlet(np.ones(n))  # mass on the -inf entries
+    got2, grad2, _ = kl.kl_to_softmax(p2, x)
+    assert got2 == np.inf
+    assert np.isfinite(grad2).all() and np.allclose(grad2[dead], -p2[dead], rtol=0, atol=0)
