@@ -192,6 +192,25 @@ int dsa_sparse_mla_decode(const dsa_queries *queries, const dsa_kv_layout *layou
                           const int32_t *count, int32_t k, float softmax_scale,
                           float *out, float *lse, void *ws, size_t ws_bytes,
                           hipStream_t stream);
+/* dsa_sparse_mla_decode for callers that cannot allocate device memory or
+ * pass a workspace (code under HIP graph capture, serving loops that forbid
+ * allocation).  The split partials go to a scratch array inside the library,
+ * DSA_NOALLOC_SCRATCH_BYTES on each GPU it runs on, held from module load
+ * until the process ends; the call itself allocates and frees nothing.
+ * Arguments and results as for dsa_sparse_mla_decode (same kernels, same
+ * values), without ws.  The stream must belong to the current device.
+ * Returns DSA_ERR_UNSUPPORTED, launching nothing, when this call's partials
+ * (dsa_workspace_bytes(DSA_OP_MLA_DECODE, queries, k)) exceed the scratch:
+ * for example 64 queries at k = 2048 fit (4 splits, 64.1 MiB), 285 queries
+ * (2 splits, 142.8 MiB) do not.  Every call on one GPU shares that GPU's
+ * scratch, which keeps the last call's contents: calls that overlap in time
+ * on one GPU (on different streams, or unordered across threads) race and
+ * give wrong results; order them on one stream. */
+#define DSA_NOALLOC_SCRATCH_BYTES ((size_t)72 << 20)
+int dsa_sparse_mla_decode_noalloc(const dsa_queries *queries, const dsa_kv_layout *layout,
+                                  const uint16_t *q, const uint16_t *kv, const int32_t *idx,
+                                  const int32_t *count, int32_t k, float softmax_scale,
+                                  float *out, float *lse, hipStream_t stream);
 /* Dense mode: the same attention over every visible position [0, q_nvis[i])
  * of each query, with no indexer and no selection.  It is the pages'
  * short-context variant (page "arXiv'25 | DSA ...", section 6: short prefill

@@ -16,13 +16,13 @@ import torch
 from . import _lib
 from ._lib import (  # noqa: F401
     DSA_D, DSA_DI, DSA_DV, DSA_H, DSA_HI, DSA_KMAX, DSA_OP_FORWARD, DSA_OP_MLA_DECODE,
-    DSA_OP_MLA_DENSE, DSA_OP_MLA_PREFILL, DSA_OP_TOPK, DsaError, KvLayoutC, QueriesC,
+    DSA_NOALLOC_SCRATCH_BYTES, DSA_OP_MLA_DENSE, DSA_OP_MLA_PREFILL, DSA_OP_TOPK, DsaError, KvLayoutC, QueriesC,
 )
 
 __all__ = [
     "HipEvents", "Queries", "KvLayout", "dsa_quantize_fp8", "dsa_quantize_fp8_e8m0", "dsa_indexer_scores",
     "dsa_indexer_scores_e8m0", "dsa_topk",
-    "dsa_sparse_mla_decode", "dsa_sparse_mla_prefill", "dsa_dense_mla", "dsa_indexer_kl_sparse",
+    "dsa_sparse_mla_decode", "dsa_sparse_mla_decode_noalloc", "dsa_sparse_mla_prefill", "dsa_dense_mla", "dsa_indexer_kl_sparse",
     "dsa_indexer_kl_dense", "dsa_indexer_backward", "dsa_forward", "dsa_workspace_bytes",
     "workspace", "lib_path",
 ]
@@ -216,6 +216,26 @@ def dsa_sparse_mla_decode(queries, layout, q, kv, idx, count, k, softmax_scale, 
                           stream=None):
     return _mla("dsa_sparse_mla_decode", DSA_OP_MLA_DECODE, queries, layout, q, kv, idx, count, k,
                 softmax_scale, out, lse, ws, stream)
+
+
+def dsa_sparse_mla_decode_noalloc(queries, layout, q, kv, idx, count, k, softmax_scale, out, lse=None,
+                                  stream=None):
+    """dsa_sparse_mla_decode with its split partials in the library's own
+    scratch (no workspace, nothing allocated; calls on one GPU must not
+    overlap)."""
+    nq = queries.num_q
+    _need(q, torch.bfloat16, (nq, DSA_H, DSA_D), "q")
+    _need(kv, torch.bfloat16, (layout.num_rows, DSA_D), "kv")
+    _need(idx, torch.int32, (nq, k), "idx")
+    if count is not None:
+        _need(count, torch.int32, (nq,), "count")
+    _need(out, torch.float32, (nq, DSA_H, DSA_DV), "out")
+    if lse is not None:
+        _need(lse, torch.float32, (nq, DSA_H), "lse")
+    qc, lc = queries.c(), layout.c()
+    _lib.check("dsa_sparse_mla_decode_noalloc", _lib.lib().dsa_sparse_mla_decode_noalloc(
+        ctypes.byref(qc), ctypes.byref(lc), _ptr(q), _ptr(kv), _ptr(idx), _ptr(count), k, float(softmax_scale),
+        _ptr(out), _ptr(lse), _stream(stream)))
 
 
 def dsa_sparse_mla_prefill(queries, layout, q, kv, idx, count, k, softmax_scale, out, lse=None, ws=None,

@@ -5,6 +5,7 @@
 #include <climits>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "dsa.h"
@@ -138,6 +139,36 @@ int mla_common(bool decode, const dsa_queries *qr, const dsa_kv_layout *ly, cons
   return hip_status(dsa::launch_mla(a, decode, ws, stream), "sparse MLA launch");
 }
 
+// Scratch of dsa_sparse_mla_decode_noalloc: the split partials live in this
+// file-scope device array instead of a caller workspace.  Each GPU holds its
+// own copy (at its own address) from module load until the process ends.  In
+// host code `scratch` only names the symbol: its device address comes from
+// hipGetSymbolAddress, once per device with that device current, and only
+// that address is ever passed to a kernel.
+static __device__ __align__(256) unsigned char scratch[DSA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[MAX_DEVICES];
+
+// Device address of the current device's scratch (nullptr and a status on failure).
+int scratch_of_current_device(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(DSA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= MAX_DEVICES) return fail(DSA_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, MAX_DEVICES);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(DSA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return DSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -221,6 +252,23 @@ int dsa_sparse_mla_decode(const dsa_queries *qr, const dsa_kv_layout *ly, const 
                           const int32_t *idx, const int32_t *count, int32_t k, float softmax_scale, float *out,
                           float *lse, void *ws, size_t ws_bytes, hipStream_t stream) {
   return mla_common(true, qr, ly, q, kv, idx, count, k, softmax_scale, out, lse, ws, ws_bytes, stream);
+}
+
+int dsa_sparse_mla_decode_noalloc(const dsa_queries *qr, const dsa_kv_layout *ly, const uint16_t *q,
+                                  const uint16_t *kv, const int32_t *idx, const int32_t *count, int32_t k,
+                                  float softmax_scale, float *out, float *lse, hipStream_t stream) {
+  int st;
+  if ((st = check_queries(qr)) || (st = check_k(k))) return st;
+  const size_t need = dsa::mla_ws_bytes(qr->num_q, k, true);
+  if (need > DSA_NOALLOC_SCRATCH_BYTES)
+    return fail(DSA_ERR_UNSUPPORTED,
+                "dsa_sparse_mla_decode_noalloc: %d queries at k = %d need %zu bytes of split partials; the "
+                "library's scratch holds %zu (use dsa_sparse_mla_decode with a workspace)",
+                qr->num_q, k, need, (size_t)DSA_NOALLOC_SCRATCH_BYTES);
+  void *ws = nullptr;
+  if (need > 0 && (st = scratch_of_current_device(&ws))) return st;
+  return mla_common(true, qr, ly, q, kv, idx, count, k, softmax_scale, out, lse, ws,
+                    need > 0 ? (size_t)DSA_NOALLOC_SCRATCH_BYTES : 0, stream);
 }
 
 int dsa_sparse_mla_prefill(const dsa_queries *qr, const dsa_kv_layout *ly, const uint16_t *q, const uint16_t *kv,

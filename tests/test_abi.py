@@ -236,3 +236,19 @@ def test_binding_rejects_block_table_rows_short_of_num_seqs(host_as_device):
         with pytest.raises(ValueError, match="block_table"):
             lay.c()
     dsa.KvLayout(2, 256, block_table=torch.zeros((2, 4), dtype=torch.int32), block_size=64).c()
+
+
+def test_noalloc_decode_refuses_partials_beyond_its_scratch():
+    """Host-side: 285 queries at k = 2048 need 2 splits of fp32 partials,
+    142.8 MiB, more than the library's scratch; refused before any launch."""
+    L = _lib.lib()
+    q = _queries(285, 4096)
+    p = ctypes.c_void_p(0x1000)
+    lay = _lib.KvLayoutC(285, 0, 0, 0, 285 * 4096, None, p.value)
+    need = L.dsa_workspace_bytes(_lib.DSA_OP_MLA_DECODE, ctypes.byref(q), 2048)
+    assert need > _lib.DSA_NOALLOC_SCRATCH_BYTES
+    st = L.dsa_sparse_mla_decode_noalloc(ctypes.byref(q), ctypes.byref(lay), p, p, p, None, 2048, 0.07, p, None,
+                                         None)
+    assert st == _lib.DSA_ERR_UNSUPPORTED and b"scratch" in L.dsa_last_error()
+    assert L.dsa_sparse_mla_decode_noalloc(ctypes.byref(q), ctypes.byref(lay), p, p, p, None, 0, 0.07, p, None,
+                                           None) == _lib.DSA_ERR_INVALID_ARG
