@@ -10,13 +10,19 @@ the timed region) and the CPU oracle timed on a bounded sample of the same
 workload.  Per-stage figures and a causal-prefill measurement (16384 tokens)
 ride along under "stages" and "prefill".
 
-    python bench.py [--steps K] [--warmup W] [--workload decode|prefill]
-                    [--no-prefill] [--no-cpu-baseline] [--cpu-sample N] [--copy-calib]
+    python bench.py [--steps K] [--warmup W]
+                    [--workload decode|prefill|decode1x4k|decode16x32k|ragged|crossover|kl]
+                    [--no-prefill] [--no-configs] [--no-cpu-baseline] [--cpu-sample N] [--copy-calib]
 
---workload prefill makes the 16384-token causal prefill the measured workload
-(used to profile it on its own).  --copy-calib runs, after the timed steps, a
-plain 1 GiB device-to-device elementwise copy whose HBM counter readings give
-the scale for the counter-based traffic figure.
+The default line also carries, under "configs", the other decode workloads:
+one query over 4096 positions (microseconds per call), 16 sequences of 32768
+(planted keys) and the ragged paged batch of 128 sequences (log-uniform lengths
+1024..131072, 64-token blocks in a random physical order) beside the same
+lengths in contiguous caches; and, under "prefill", the 16384-token causal
+prefill with its own sampled CPU-oracle baseline.  --workload <name> makes one
+of them the measured line (used to profile it on its own).  --copy-calib runs,
+after the timed steps, a plain 1 GiB device-to-device elementwise copy whose
+HBM counter readings give the scale for the counter-based traffic figure.
 """
 
 import argparse
@@ -80,6 +86,49 @@ def mla_work(counts):
     flops = rows * 128 * (576 + 512) * 2
     gather = rows * 1152
     return rows, flops, gather
+
+
+def decode_bytes(wl):
+    """Algorithmic bytes (and the attention's flops) of one dsa_forward on a
+    decode-style workload: the indexer reads each scored key row (128 B), its
+    scale (4 B) and writes its score (4 B), plus q, w and q_scale per scored
+    query; the top-k reads the scores and writes k positions per query; the
+    attention gathers 1152 B per selected row and reads q (144 KiB), writes
+    out (256 KiB) and reads k positions per query."""
+    nv = wl.q_nvis.cpu().numpy()
+    k = wl.k
+    units = indexer_units(nv, k)
+    scored = int((nv > k).sum())
+    rows, flops, gather = mla_work(np.minimum(nv, k))
+    return {"indexer": units * IDX_BYTES_PER_KEY + scored * (64 * 128 + 64 * 8),
+            "topk": units * 4 + wl.nq * k * 4,
+            "mla": gather + wl.nq * (128 * 576 * 2 + 128 * 512 * 4 + k * 4),
+            "mla_flops": flops, "mla_gather": gather, "keys_scored": units, "rows_attended": rows}
+
+
+def planted_in_topk(wl, idx):
+    """How many of each sequence's planted key positions the forward selected
+    (decode: query i is sequence i)."""
+    if not wl.planted:
+        return None
+    idx_h = idx.cpu().numpy()
+    q_seq = wl.q_seq.cpu().numpy()
+    hits, per_seq = [], []
+    for s, pos in sorted(wl.planted.items()):
+        qi = int(np.nonzero(q_seq == s)[0][-1])
+        sel = idx_h[qi][idx_h[qi] >= 0]
+        hits.append(int(np.isin(pos, sel).sum()))
+        per_seq.append(len(pos))
+    hits = np.asarray(hits)
+    return {"planted_per_sequence": int(np.max(per_seq)), "selected_per_sequence_mean": float(hits.mean()),
+            "selected_min": int(hits.min()), "selected_max": int(hits.max()),
+            "share_of_planted_selected": float(hits.sum() / max(1, int(np.sum(per_seq)))),
+            "share_of_topk_that_is_planted": float(hits.mean() / wl.k)}
+
+
+def flush_caches(buf):
+    """Evicts L2 and the 256 MB Infinity Cache: writes a 1 GiB buffer."""
+    buf.fill_(1.0)
 
 
 def prepare(wl):
@@ -146,6 +195,89 @@ def time_forward(wl, p, steps, warmup):
         st["mla"].append(ev.elapsed_ms(4 * i + 2, 4 * i + 3))
     ev.close()
     return wall, {k: float(np.mean(v)) for k, v in st.items()}, wall_ev
+
+
+def time_forward_cold(wl, p, steps):
+    """Mean ms of one dsa_forward with L2 and the Infinity Cache flushed before
+    each step: torch events around each step on the stream the library
+    launches on (the current stream), the flush outside them."""
+    import sparse_long_context_dsa_amd as dsa
+    buf = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for e0, e1 in evs:
+        flush_caches(buf)
+        e0.record()
+        dsa.dsa_forward(p["queries"], p["layout"], p["q8"], p["qs"], wl.w, p["k8"], p["ks"], wl.q_mla, wl.kv,
+                        wl.k, wl.softmax_scale, p["out"], p["lse"], p["idx"], ws=p["ws"])
+        e1.record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    del buf
+    return ms
+
+
+def measure_decode(wl, steps, warmup, cold=False):
+    """One decode workload: warm steps (wall clock, then HIP events between
+    the stages), optionally cold steps, the HBM fractions of each stage and of
+    the whole step, and the planted-key diagnostic."""
+    p = prepare(wl)
+    torch.cuda.synchronize()
+    wall, st, wall_ev = time_forward(wl, p, steps, warmup)
+    b = decode_bytes(wl)
+    ms = 1e3 * wall / steps
+    total = b["indexer"] + b["topk"] + b["mla"]
+    res = {
+        "workload": wl.name, "batch": wl.nq, "context_max": int(wl.q_nvis.max().item()),
+        "context_mean": float(wl.q_nvis.float().mean().item()), "k": wl.k,
+        "paged_block_size": wl.block_size or None,
+        "queries_per_s": wl.nq * steps / wall, "ms_per_step": ms, "us_per_step": 1e3 * ms,
+        "events_pass_ms_per_step": 1e3 * wall_ev / steps,
+        "indexer_ms": st["indexer"], "topk_ms": st["topk"], "mla_ms": st["mla"],
+        "algorithmic_bytes": {kk: b[kk] for kk in ("indexer", "topk", "mla")},
+        "step_gbs": total / (ms * 1e-3) / 1e9, "step_frac_hbm": total / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "roofline_queries_per_s": wl.nq / (total / (HBM_PEAK_GBS * 1e9)),
+        "mla_tflops_bf16": b["mla_flops"] / (st["mla"] * 1e-3) / 1e12,
+    }
+    for stage in ("indexer", "topk", "mla"):
+        if st[stage] > 0 and b[stage] > 0:
+            res[f"{stage}_frac_hbm"] = b[stage] / (st[stage] * 1e-3) / 1e9 / HBM_PEAK_GBS
+    if cold:
+        cms = time_forward_cold(wl, p, steps)
+        res["cold_ms_per_step"] = cms
+        res["cold_us_per_step"] = 1e3 * cms
+        res["cold_queries_per_s"] = wl.nq / (cms * 1e-3)
+    res["planted"] = planted_in_topk(wl, p["idx"])
+    del p
+    torch.cuda.empty_cache()
+    return res
+
+
+def extra_decode_configs(steps, warmup):
+    """The decode workloads beside the headline: 1 x 4096 (latency), 16 x 32768
+    (planted) and the ragged paged batch, the latter also with the same
+    lengths in contiguous caches (the cost of paging)."""
+    from workloads import make_config, make_custom
+    out = {}
+    for cfg, key, cold in ((0, "decode_1x4096", True), (1, "decode_16x32768_planted", True),
+                           (4, "ragged_paged_128", True)):
+        log(f"config: {key}")
+        wl = make_config(cfg, device="cuda")
+        out[key] = measure_decode(wl, steps, warmup, cold=cold)
+        if cfg == 4:
+            lens = wl.seq_len.tolist()
+            del wl
+            torch.cuda.empty_cache()
+            log("config: the same ragged lengths, contiguous caches")
+            wl = make_custom(seq_lens=lens, device="cuda", seed=20260004, name="ragged contiguous 128")
+            c = measure_decode(wl, steps, warmup, cold=True)
+            out["ragged_contiguous_128"] = c
+            pg = out[key]
+            out[key]["paging_cost"] = {"warm": pg["ms_per_step"] / c["ms_per_step"] - 1.0,
+                                       "cold": pg["cold_ms_per_step"] / c["cold_ms_per_step"] - 1.0}
+        del wl
+        torch.cuda.empty_cache()
+    return out
 
 
 def key_scale_formats(wl, p, steps):
@@ -219,7 +351,56 @@ def cpu_baseline(wl, sample, k):
                       f"attention per query), {dt:.1f} s"}
 
 
-def run_prefill(steps, warmup):
+def prefill_cpu_baseline(wl, k, n_random=250, seed=5):
+    """The oracle on a stratified sample of the causal prefill's queries: the
+    positions t = 1, 2, 2048, 2049, 2050 and 16383 (0-based, n_vis = t) plus
+    n_random seeded random positions, each a whole indexer -> top-k -> sparse
+    attention query.  The full prefill's oracle time is extrapolated from the
+    sample by flop share (indexer 2*64*128 flop per scored key, attention
+    2*128*1088 flop per attended row) and reported as tokens/s, labelled as
+    extrapolated.  Inputs are prepared outside the timed region."""
+    import oracle
+    nv = wl.q_nvis.cpu().numpy()
+    n = wl.nq
+    fixed = [t for t in (1, 2, 2048, 2049, 2050, n - 1) if t < n]
+    rng = np.random.default_rng(seed)
+    rest = np.setdiff1d(np.arange(n), fixed)
+    sample = sorted(set(fixed) | set(rng.choice(rest, min(n_random, rest.size), replace=False).tolist()))
+    log(f"prefill cpu baseline: preparing {len(sample)} queries")
+    k8_all, ks_all = oracle.quantize_rows(wl.k_idx.cpu().numpy())
+    kv_all = wl.kv.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    row0 = int(wl.row0[0].item())
+
+    def flops(t):
+        t = int(t)
+        return (2 * 64 * 128 * t if t > k else 0) + 2 * 128 * 1088 * min(k, t)
+
+    inputs = []
+    for i in sample:
+        t = int(nv[i])
+        q8, qs = oracle.quantize_rows(wl.q_idx[i].cpu().numpy())
+        qm = wl.q_mla[i].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        inputs.append((q8, qs, wl.w[i].cpu().numpy(), k8_all[row0:row0 + t], ks_all[row0:row0 + t], qm,
+                       kv_all[row0:row0 + t]))
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([int(x.get("num_threads", 1)) for x in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        cores = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    for args in inputs:
+        oracle.forward_query(*args, k, wl.softmax_scale)
+    dt = time.perf_counter() - t0
+    share = sum(flops(nv[i]) for i in sample) / sum(flops(t) for t in nv)
+    est = dt / share
+    return {"value": n / est, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{len(sample)} of the {n} causal prefill queries (t = {fixed} and {len(sample) - len(fixed)} "
+                      f"seeded random t; full indexer, top-k and attention per query) in {dt:.1f} s, "
+                      f"extrapolated to the whole prefill by flop share ({share:.4f} of its flops): "
+                      f"{est:.0f} s estimated"}
+
+
+def run_prefill(steps, warmup, cpu=False):
     from workloads import make_config
     log("prefill: generating 16384-token causal workload")
     wl = make_config(3, device="cuda")
@@ -243,9 +424,14 @@ def run_prefill(steps, warmup):
         "mla_tflops_bf16": flops / (st["mla"] * 1e-3) / 1e12,
         "mla_frac_bf16_peak": flops / (st["mla"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
         "mla_gather_gbs": gather / (st["mla"] * 1e-3) / 1e9,
+        "topk_gbs": (pairs * 4 + wl.nq * wl.k * 4) / (st["topk"] * 1e-3) / 1e9 if st["topk"] > 0 else None,
     }
-    del wl, p
+    del p
     torch.cuda.empty_cache()
+    if cpu:
+        log("prefill: timing the CPU oracle on a stratified sample")
+        res["cpu_baseline"] = prefill_cpu_baseline(wl, wl.k)
+    del wl
     return res
 
 
@@ -255,7 +441,7 @@ def common_fields(args):
 
 
 def prefill_result(args):
-    pf = run_prefill(args.steps, args.warmup)
+    pf = run_prefill(args.steps, args.warmup, cpu=not args.no_cpu_baseline)
     mla_achieved = pf["mla_tflops_bf16"]
     result = {"metric": "DSA layer prefill tokens/s (16384-token causal sequence)",
               "value": pf["tokens_per_s"], "unit": "tokens/s"}
@@ -269,6 +455,28 @@ def prefill_result(args):
                      "traffic": None},
         "stages": pf,
     })
+    if "cpu_baseline" in pf:
+        result["cpu_baseline"] = pf.pop("cpu_baseline")
+    return result
+
+
+def config_result(args, cfg, key):
+    """One of the other decode workloads as the measured line."""
+    from workloads import make_config
+    log(f"config: {key}")
+    wl = make_config(cfg, device="cuda")
+    r = measure_decode(wl, args.steps, args.warmup, cold=True)
+    result = {"metric": f"DSA layer decode queries/s ({r['workload']})", "value": r["queries_per_s"],
+              "unit": "queries/s"}
+    result.update(common_fields(args))
+    result.update({
+        "ms_per_step": r["ms_per_step"],
+        "config": {"workload": r["workload"], "batch": r["batch"], "context": r["context_max"], "k": r["k"],
+                   "indexer_heads": 64, "indexer_dim": 128, "heads": 128, "latent": 576},
+        "roofline": {"bound": "hbm", "kernel": "indexer", "achieved": r["algorithmic_bytes"]["indexer"] /
+                     (r["indexer_ms"] * 1e-3) / 1e9 if r["indexer_ms"] > 0 else None, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": r.get("indexer_frac_hbm"), "traffic": None},
+        "stages": r})
     return result
 
 
@@ -321,6 +529,7 @@ def decode_result(args):
     })
     if traffic is not None:
         result["roofline"]["traffic_bytes_per_launch"] = INDEXER_TRAFFIC["bytes_per_launch"]
+    result["stages"]["planted"] = planted_in_topk(wl, p["idx"])
     log("standalone indexer: fp32 vs E8M0 key scales")
     result["indexer_key_scales"] = key_scale_formats(wl, p, args.steps)
     if args.copy_calib:
@@ -332,8 +541,10 @@ def decode_result(args):
     del p
     del wl
     torch.cuda.empty_cache()
+    if not args.no_configs:
+        result["configs"] = extra_decode_configs(args.steps, args.warmup)
     if not args.no_prefill:
-        result["prefill"] = run_prefill(max(2, args.steps // 4), 2)
+        result["prefill"] = run_prefill(max(2, args.steps // 4), 2, cpu=not args.no_cpu_baseline)
     return result
 
 
@@ -494,10 +705,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", choices=("decode", "prefill", "crossover", "kl"), default="decode")
+    ap.add_argument("--workload", choices=("decode", "prefill", "decode1x4k", "decode16x32k", "ragged", "crossover",
+                                           "kl"), default="decode")
     ap.add_argument("--cpu-sample", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-configs", action="store_true")
     ap.add_argument("--copy-calib", action="store_true")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -514,6 +727,10 @@ def main():
         result = crossover_result(args)
     elif args.workload == "kl":
         result = kl_result(args)
+    elif args.workload in ("decode1x4k", "decode16x32k", "ragged"):
+        cfg, key = {"decode1x4k": (0, "decode_1x4096"), "decode16x32k": (1, "decode_16x32768_planted"),
+                    "ragged": (4, "ragged_paged_128")}[args.workload]
+        result = config_result(args, cfg, key)
     elif args.workload == "prefill":
         result = prefill_result(args)
         if args.copy_calib:
