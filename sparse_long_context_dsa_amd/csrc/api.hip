@@ -92,14 +92,21 @@ struct FwdWs {
 
 int64_t fwd_ld(const dsa_queries *qr) { return ((int64_t)qr->max_nvis + 63) / 64 * 64; }
 
+// The indexer selects the rows itself (scores never leave the chip) when one
+// of its blocks covers each query's whole history.
+bool fwd_selects_in_indexer(const dsa_queries *qr, int32_t k) {
+  return qr->max_nvis > k && dsa::indexer_selects(qr->num_q, qr->max_nvis);
+}
+
 size_t fwd_bytes(const dsa_queries *qr, int32_t k, FwdWs *out, void *base) {
   const size_t nq = (size_t)qr->num_q;
   const int64_t ld = fwd_ld(qr);
+  const bool sel = fwd_selects_in_indexer(qr, k);
   size_t off = 0;
-  const size_t s_scores = align256(nq * (size_t)ld * 4);
+  const size_t s_scores = sel ? 0 : align256(nq * (size_t)ld * 4);
   const size_t s_idx = align256(nq * (size_t)k * 4);
   const size_t s_cnt = align256(nq * 4);
-  const size_t s_topk = align256(dsa::topk_ws_bytes(qr->num_q, qr->max_nvis));
+  const size_t s_topk = sel ? 0 : align256(dsa::topk_ws_bytes(qr->num_q, qr->max_nvis));
   const bool decode = true;
   const size_t s_mla = align256(dsa::mla_ws_bytes(qr->num_q, k, decode));
   if (out) {
@@ -388,19 +395,27 @@ static int forward_impl(const dsa_queries *qr, const dsa_kv_layout *ly, const ui
   auto mark = [&](int i) {
     if (events && events[i] && e == hipSuccess) e = hipEventRecord(events[i], stream);
   };
-  if (qr->max_nvis > k) e = dsa::launch_topk_init(tw, qr->num_q, stream);
+  const bool sel = fwd_selects_in_indexer(qr, k);
+  if (qr->max_nvis > k && !sel) e = dsa::launch_topk_init(tw, qr->num_q, stream);
   mark(0);
-  if (qr->max_nvis > k) {
-    if (e == hipSuccess) {
+  if (sel) {
+    // Every query's history fits one indexer block: the indexer writes the
+    // positions (and the short histories' full lists); no scores, no top-k launch.
+    dsa::IndexerLaunch ia{q_fp8, q_scale, w, k_fp8, k_scale, qr->q_seq, qr->q_nvis, m, nullptr, 0,
+                          nullptr, k, qr->num_q, qr->max_nvis, nullptr, idx, fw.count, k};
+    if (e == hipSuccess) e = dsa::launch_indexer(ia, stream);
+    mark(1);
+  } else {
+    if (qr->max_nvis > k && e == hipSuccess) {
       dsa::IndexerLaunch ia{q_fp8, q_scale, w, k_fp8, k_scale, qr->q_seq, qr->q_nvis, m, fw.scores, fw.ld,
                             tw.hist, k, qr->num_q, qr->max_nvis};
       e = dsa::launch_indexer(ia, stream);
     }
+    mark(1);
+    if (e == hipSuccess)
+      e = dsa::launch_topk_select(fw.scores, fw.ld, qr->q_nvis, k, idx, fw.count, tw, qr->num_q, qr->max_nvis,
+                                  true, stream);
   }
-  mark(1);
-  if (e == hipSuccess)
-    e = dsa::launch_topk_select(fw.scores, fw.ld, qr->q_nvis, k, idx, fw.count, tw, qr->num_q, qr->max_nvis, true,
-                                stream);
   mark(2);
   if (e == hipSuccess) {
     dsa::MlaLaunch ma{q, kv, idx, fw.count, qr->q_seq, qr->q_nvis, m, k, qr->num_q, softmax_scale, out, lse,

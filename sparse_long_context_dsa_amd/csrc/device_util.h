@@ -54,6 +54,17 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Workgroup barrier for LDS traffic only: waits for this wavefront's LDS
+// operations, not for its outstanding global loads (which __syncthreads'
+// release fence would also wait for), so loads issued earlier keep flying.
+// Use only where the threads exchange data through LDS.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave.
 __device__ __forceinline__ int wave_inclusive_scan(int v) {
   const int lane = threadIdx.x & (WAVE - 1);

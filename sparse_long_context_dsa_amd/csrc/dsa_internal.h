@@ -45,7 +45,17 @@ struct IndexerLaunch {
   int32_t num_q;
   int32_t max_nvis;
   const uint8_t *k_e8m0;  // key scales as E8M0 exponents instead of k_scale (null: use k_scale)
+  // Select in the indexer (only when indexer_selects(num_q, max_nvis)): the
+  // scores stay on chip and each block writes its query's top-k positions
+  // idx[q, 0 .. sel_k) and count[q]; hist must be null.  Queries with
+  // n_vis <= skip_le keep every position.
+  int32_t *sel_idx;
+  int32_t *sel_count;
+  int32_t sel_k;
 };
+// Whether one indexer block covers every query's whole history, so that the
+// indexer can select the rows itself.
+bool indexer_selects(int num_q, int max_nvis);
 hipError_t launch_indexer(const IndexerLaunch &a, hipStream_t st);
 
 // Top-k: radix digits of 11/11/10 bits; rows up to TOPK_ROW_MAX are selected
@@ -59,11 +69,13 @@ constexpr int MAX_NVIS = TOPK_CHUNK * TOPK_MAX_CHUNKS;
 constexpr int TOPK_LONG_WAVES = 16;    // wavefronts of a long-row block
 constexpr int TOPK_WAVE_SPAN = 2048;   // positions per wavefront (4 rounds of 512)
 constexpr int TOPK_LONG_SPAN = TOPK_LONG_WAVES * TOPK_WAVE_SPAN;  // 32768 positions per block
+constexpr int TOPK_STREAM_MAX = 131072;  // rows up to this length: one streaming block per row
 struct TopkWs {
   uint32_t *hist;     // [num_q, TOPK_BINS] first-digit histogram (cleared each call)
   uint2 *b1info;      // [num_q] long rows: (first-digit threshold bin B1, keys above B1)
   uint32_t *wcnt;     // [num_q, nblk, TOPK_LONG_WAVES] candidates per wavefront
   uint2 *cand;        // [num_q, nblk, TOPK_LONG_WAVES, TOPK_WAVE_SPAN] (key, position)
+  uint32_t *hist2;    // [num_q, nblk, TOPK_BINS] per span: second-digit histogram of its keys in bin B1
   int32_t nblk;       // long-row blocks per query (0 when every row fits TOPK_ROW_MAX)
   int32_t nchunks;    // score chunks per row for the standalone histogram
 };

@@ -31,8 +31,13 @@
 // Optionally each block also builds a 2048-bin histogram of the top 11 bits
 // of the scores' order-preserving keys (the first pass of the top-k radix
 // select), so the top-k stage need not read the scores twice.
-#include "device_util.h"
-#include "dsa_internal.h"
+//
+// When one block covers a query's whole history (up to 16384 positions: many
+// queries, as in causal prefill), the block can instead select the row itself
+// (page "arXiv'25 | DSA ...", section 3, second equation): the scores stay in
+// LDS, the first-digit histogram is built there as they are produced, and
+// the block's radix select writes the positions; no score leaves the CU.
+#include "topk_row.h"
 
 namespace dsa {
 
@@ -84,26 +89,34 @@ __device__ __forceinline__ float relu(float x) {
   return r;
 }
 
-template <bool HIST, bool E8M0>
+template <bool HIST, bool E8M0, bool SEL>
 // Three wavefronts per SIMD: the epilogue of key tile t overlapping tile
 // t + 1's MFMAs needs 16 more registers than a serial epilogue, and left to
 // itself the compiler would spend them on accumulator registers and drop to
-// two wavefronts.
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void indexer_kernel(IndexerLaunch a,
-                                                                                               int nchunks, int kpw) {
+// two wavefronts.  (SEL: the 72 KiB of LDS leave room for two blocks per CU.)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SEL ? 2 : 3, SEL ? 2 : 3))) void indexer_kernel(
+    IndexerLaunch a, int nchunks, int kpw) {
+  static_assert(!(HIST && SEL), "a selecting block keeps its histogram in LDS");
   const int q = blockIdx.x / nchunks;
   const int chunk = blockIdx.x - q * nchunks;
   const int nvis = a.q_nvis[q];
+  if (SEL && nvis <= a.skip_le) {  // short history: every position is kept (block-uniform)
+    for (int i = threadIdx.x; i < a.sel_k; i += blockDim.x) a.sel_idx[(int64_t)q * a.sel_k + i] = i < nvis ? i : -1;
+    if (threadIdx.x == 0) a.sel_count[q] = nvis;
+    return;
+  }
   if (nvis <= a.skip_le || chunk * IDX_WAVES * kpw >= nvis) return;  // block-uniform
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int seq = a.q_seq[q];
 
-  __shared__ uint32_t hist[HIST ? TOPK_BINS : 1];
+  __shared__ uint32_t hist[(HIST || SEL) ? TOPK_BINS : 1];
   // Per-wavefront staging of 256 scores: written as 16-byte stores (1 KiB per
   // wavefront instruction), which the memory system takes much better than
   // one 256-byte store per 64 keys.
-  __shared__ __attribute__((aligned(16))) float sbuf[IDX_WAVES][256];
-  if (HIST) {
+  __shared__ __attribute__((aligned(16))) float sbuf[SEL ? 1 : IDX_WAVES][256];
+  // SEL: the whole row's scores, by position.
+  __shared__ __attribute__((aligned(16))) float rowbuf[SEL ? TOPK_ROW_MAX : 4];
+  if (HIST || SEL) {
     for (int b = threadIdx.x; b < TOPK_BINS; b += blockDim.x) hist[b] = 0u;
     __syncthreads();
   }
@@ -197,6 +210,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     const float x0 = swap_sum<false>(p[0], p[2]);
     const float x1 = swap_sum<false>(p[1], p[3]);
     const float score = swap_sum<true>(x0, x1) * cur.ks;
+    if (SEL) {
+      if (s0 + lane < s_end) {
+        rowbuf[s0 + lane] = score;
+        atomicAdd(&hist[order_key(score) >> 21], 1u);
+      }
+      return;
+    }
     const int j = ((s0 - s_begin) >> 6) & 3;  // step within the 256-key group
     sbuf[wave][64 * j + lane] = score;
     // Lane l stores keys g0 + 4l .. g0 + 4l + 3 of the group.
@@ -221,6 +241,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   }
   if (pending >= 0) flush(pending);
 
+  if (SEL) {  // the row's scores and first-digit histogram are in LDS
+    __shared__ int sm[IDX_WAVES];
+    __shared__ uint64_t sm64[IDX_WAVES];
+    __shared__ int res[2];
+    __syncthreads();
+    select_row<IDX_WAVES * WAVE>(rowbuf, nvis, a.sel_k, HIST_LDS, nullptr, hist, sm, sm64, res,
+                                 a.sel_idx + (int64_t)q * a.sel_k, a.sel_count + q);
+    return;
+  }
+
   if (HIST) {
     __syncthreads();
     uint32_t *gh = a.hist + (int64_t)q * TOPK_BINS;
@@ -231,31 +261,47 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
   }
 }
 
-hipError_t launch_indexer(const IndexerLaunch &a, hipStream_t st) {
-  if (a.num_q == 0 || a.max_nvis == 0) return hipSuccess;
-  // The longest run per wavefront that still gives the chip enough
-  // wavefronts: long runs amortise each wavefront's set-up (its query's q,
-  // weights and histogram), short ones keep enough loads in flight when only
-  // a few queries stream long histories from HBM.
+// The longest run per wavefront that still gives the chip enough wavefronts:
+// long runs amortise each wavefront's set-up (its query's q, weights and
+// histogram), short ones keep enough loads in flight when only a few queries
+// stream long histories from HBM.
+static int indexer_kpw(int num_q, int max_nvis) {
   int kpw = IDX_KPW_MIN;
   while (kpw < IDX_KPW_MAX) {
-    const int64_t chunks = (a.max_nvis + IDX_WAVES * 2 * kpw - 1) / (IDX_WAVES * 2 * kpw);
-    if ((int64_t)a.num_q * chunks * IDX_WAVES < IDX_MIN_WAVES) break;
+    const int64_t chunks = (max_nvis + IDX_WAVES * 2 * kpw - 1) / (IDX_WAVES * 2 * kpw);
+    if ((int64_t)num_q * chunks * IDX_WAVES < IDX_MIN_WAVES) break;
     kpw *= 2;
   }
+  return kpw;
+}
+
+bool indexer_selects(int num_q, int max_nvis) {
+  return num_q > 0 && max_nvis > 0 && max_nvis <= TOPK_ROW_MAX &&
+         IDX_WAVES * indexer_kpw(num_q, max_nvis) >= max_nvis;
+}
+
+hipError_t launch_indexer(const IndexerLaunch &a, hipStream_t st) {
+  if (a.num_q == 0 || a.max_nvis == 0) return hipSuccess;
+  const int kpw = indexer_kpw(a.num_q, a.max_nvis);
   const int nchunks = (a.max_nvis + IDX_WAVES * kpw - 1) / (IDX_WAVES * kpw);
+  const bool sel = a.sel_idx != nullptr;
+  if (sel && (nchunks != 1 || a.hist || !a.sel_count || a.max_nvis > TOPK_ROW_MAX)) return hipErrorInvalidValue;
   const int64_t blocks = (int64_t)a.num_q * nchunks;
   const dim3 grid((unsigned)blocks), block(IDX_WAVES * WAVE);
   if (a.k_e8m0) {
-    if (a.hist)
-      hipLaunchKernelGGL((indexer_kernel<true, true>), grid, block, 0, st, a, nchunks, kpw);
+    if (sel)
+      hipLaunchKernelGGL((indexer_kernel<false, true, true>), grid, block, 0, st, a, nchunks, kpw);
+    else if (a.hist)
+      hipLaunchKernelGGL((indexer_kernel<true, true, false>), grid, block, 0, st, a, nchunks, kpw);
     else
-      hipLaunchKernelGGL((indexer_kernel<false, true>), grid, block, 0, st, a, nchunks, kpw);
+      hipLaunchKernelGGL((indexer_kernel<false, true, false>), grid, block, 0, st, a, nchunks, kpw);
   } else {
-    if (a.hist)
-      hipLaunchKernelGGL((indexer_kernel<true, false>), grid, block, 0, st, a, nchunks, kpw);
+    if (sel)
+      hipLaunchKernelGGL((indexer_kernel<false, false, true>), grid, block, 0, st, a, nchunks, kpw);
+    else if (a.hist)
+      hipLaunchKernelGGL((indexer_kernel<true, false, false>), grid, block, 0, st, a, nchunks, kpw);
     else
-      hipLaunchKernelGGL((indexer_kernel<false, false>), grid, block, 0, st, a, nchunks, kpw);
+      hipLaunchKernelGGL((indexer_kernel<false, false, false>), grid, block, 0, st, a, nchunks, kpw);
   }
   return hipGetLastError();
 }

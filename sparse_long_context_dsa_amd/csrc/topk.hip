@@ -41,22 +41,10 @@
 //    compaction.  (Handing the row to its last block inside one kernel would
 //    need an agent-scope fence per block, which on this part writes back and
 //    invalidates the XCD's L2 and costs far more.)
-#include "device_util.h"
-#include "dsa_internal.h"
+#include "topk_finish.h"
 
 namespace dsa {
 
-constexpr int TK_THREADS = 256;                               // threads of a row block
-constexpr int TK_J = 8;                                       // scores per thread per round (two float4)
-// A block of NT threads holding one row of up to TOPK_ROW_MAX scores in
-// registers: ROUNDS rounds of TK_J consecutive scores per thread.
-template <int NT>
-struct RowShape {
-  static constexpr int ROUNDS = TOPK_ROW_MAX / (NT * TK_J);  // 8 for 256 threads, 2 for 1024
-  static constexpr int PER = ROUNDS * TK_J;                  // keys per thread
-  static constexpr int ROUND_SPAN = NT * TK_J;               // positions per round
-  static_assert(ROUNDS >= 1 && ROUNDS <= 8 && ROUNDS * NT * TK_J == TOPK_ROW_MAX, "whole rounds, <= 8");
-};
 constexpr int LONG_THREADS = TOPK_LONG_WAVES * WAVE;
 constexpr int LONG_ROUNDS = TOPK_WAVE_SPAN / 512;  // rounds of 512 positions per wavefront
 constexpr int TAIL_CAP = 12288;                     // candidates the finishing block keeps in LDS
@@ -67,21 +55,31 @@ static inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 static inline int topk_nchunks(int max_nvis) {
   return max_nvis <= TOPK_ROW_MAX ? 0 : (max_nvis + TOPK_CHUNK - 1) / TOPK_CHUNK;
 }
-static inline int topk_nblk(int max_nvis) {
-  return max_nvis <= TOPK_ROW_MAX ? 0 : (max_nvis + TOPK_LONG_SPAN - 1) / TOPK_LONG_SPAN;
+// Blocks per row of the two-kernel path; 0 selects the streaming kernel (one
+// block per row).  A row streams through one CU at only about 25 GB/s (its
+// scores mostly come from HBM), against about 21 GB/s per CU but four CUs per
+// row in the two-kernel path, which pays a second launch and a finishing
+// pass.  Measured on this part: 16 rows of 32768 (19 us) and a ragged batch
+// of 128 rows up to 131072 (33 against 48 us) favour streaming; 64 rows of
+// 131072, whose four blocks per row just fill the 256 CUs, favour the two
+// kernels (30 against 34 us).  Hence: streaming up to 32 rows and from 128 rows.
+static inline int topk_nblk(int num_q, int max_nvis) {
+  if (max_nvis <= TOPK_ROW_MAX || (max_nvis <= TOPK_STREAM_MAX && (num_q <= 32 || num_q >= 128))) return 0;
+  return (max_nvis + TOPK_LONG_SPAN - 1) / TOPK_LONG_SPAN;
 }
 
 size_t topk_ws_bytes(int num_q, int max_nvis) {
-  const size_t nq = (size_t)num_q, nb = (size_t)topk_nblk(max_nvis);
+  const size_t nq = (size_t)num_q, nb = (size_t)topk_nblk(num_q, max_nvis);
   return align256(nq * TOPK_BINS * 4) + align256(nq * sizeof(uint2)) +
-         align256(nq * nb * TOPK_LONG_WAVES * 4) + nq * nb * TOPK_LONG_SPAN * sizeof(uint2);
+         align256(nq * nb * TOPK_LONG_WAVES * 4) + align256(nq * nb * TOPK_BINS * 4) +
+         nq * nb * TOPK_LONG_SPAN * sizeof(uint2);
 }
 
 TopkWs topk_ws_carve(void *ws, int num_q, int max_nvis) {
   TopkWs w;
   const size_t nq = (size_t)num_q;
   w.nchunks = topk_nchunks(max_nvis);
-  w.nblk = topk_nblk(max_nvis);
+  w.nblk = topk_nblk(num_q, max_nvis);
   uint8_t *p = static_cast<uint8_t *>(ws);
   w.hist = reinterpret_cast<uint32_t *>(p);  // [nq, 2048] first digit (cleared each call)
   p += align256(nq * TOPK_BINS * 4);
@@ -89,154 +87,20 @@ TopkWs topk_ws_carve(void *ws, int num_q, int max_nvis) {
   p += align256(nq * sizeof(uint2));
   w.wcnt = reinterpret_cast<uint32_t *>(p);
   p += align256(nq * w.nblk * TOPK_LONG_WAVES * 4);
+  w.hist2 = reinterpret_cast<uint32_t *>(p);
+  p += align256(nq * w.nblk * TOPK_BINS * 4);
   w.cand = reinterpret_cast<uint2 *>(p);
   return w;
 }
 
-// ------------------------------------------------------------------ helpers
-// Exclusive scan over the block of one value per thread; `total` gets the sum.
-template <int NT, typename T>
-__device__ __forceinline__ T block_exclusive_scan(T v, T *sm, T &total) {
-  constexpr int W = NT / WAVE;
-  const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
-  T inc = v;
-#pragma unroll
-  for (int d = 1; d < WAVE; d <<= 1) {
-    const T o = __shfl_up(inc, d, WAVE);
-    if (lane >= d) inc += o;
-  }
-  if (lane == WAVE - 1) sm[wave] = inc;
-  __syncthreads();
-  T before = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < W; ++w) {
-    const T s = sm[w];
-    before += (w < wave) ? s : T(0);
-    tot += s;
-  }
-  __syncthreads();
-  total = tot;
-  return before + inc - v;
-}
-
-// Given an LDS histogram h[NB] and a rank r >= 1 counted from the top, finds
-// the bin B with above(B) < r <= above(B) + h[B] (above(B) = sum of h[b > B]).
-// res[0] = B, res[1] = above(B), visible to all threads on return.
-template <int NT, int NB>
-__device__ void find_rank_bin(const uint32_t *h, int r, int *sm, int *res) {
-  constexpr int PER = NB / NT;
-  const int hi = NB - PER * (int)threadIdx.x;  // bins [hi - PER, hi), scanned top-down
-  int local = 0;
-#pragma unroll
-  for (int i = 1; i <= PER; ++i) local += (int)h[hi - i];
-  int total;
-  int acc = block_exclusive_scan<NT>(local, sm, total);
-#pragma unroll
-  for (int i = 1; i <= PER; ++i) {
-    const int c = (int)h[hi - i];
-    if (acc < r && acc + c >= r) {
-      res[0] = hi - i;
-      res[1] = acc;
-    }
-    acc += c;
-  }
-  __syncthreads();
-}
-
-template <int NT>
-__device__ __forceinline__ void zero_lds(uint32_t *h, int n) {
-  for (int b = threadIdx.x; b < n; b += NT) h[b] = 0u;
-}
-
-// Position of key slot (round rr, element j) of thread t relative to the block start.
-template <int NT>
-__device__ __forceinline__ int slot_pos(int t, int rr, int j) {
-  return rr * RowShape<NT>::ROUND_SPAN + TK_J * t + j;
-}
-
-// Loads the scores of this thread (positions base + slot_pos).  Positions
-// >= n get key 0, below the key of any real score (even -inf maps to
-// 0x007FFFFF): key 0 sits in first-digit bin 0, which no real score occupies,
-// so it never reaches a threshold bin, never ties the k-th key and is never
-// selected; the kernels need no separate position test.
-template <int NT>
-__device__ __forceinline__ void load_keys(const float *row, int base, int n, uint32_t *key) {
-  const int t = threadIdx.x;
-#pragma unroll
-  for (int rr = 0; rr < RowShape<NT>::ROUNDS; ++rr) {
-    const int i = base + slot_pos<NT>(t, rr, 0);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int ii = i + 4 * h;
-      if (ii + 3 < n) {
-        const float4 f = *reinterpret_cast<const float4 *>(row + ii);
-        key[TK_J * rr + 4 * h + 0] = order_key(f.x);
-        key[TK_J * rr + 4 * h + 1] = order_key(f.y);
-        key[TK_J * rr + 4 * h + 2] = order_key(f.z);
-        key[TK_J * rr + 4 * h + 3] = order_key(f.w);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) key[TK_J * rr + 4 * h + j] = (ii + j < n) ? order_key(row[ii + j]) : 0u;
-      }
-    }
-  }
-}
-
-// Per-round counts (each <= TK_J) packed into two 64-bit words, so that one
-// pair of block scans orders every round.  A field must hold the block total
-// of its round, NT * TK_J: 12-bit fields (5 per word) for 256 threads (2048),
-// 32-bit fields (2 per word) for 1024 threads (8192; 2 rounds).
-struct Packed {
-  uint64_t w0, w1;
-};
-template <int NT>
-struct PackShape {
-  static constexpr int BITS = NT * TK_J < 4096 ? 12 : 32;
-  static constexpr int PER_WORD = 64 / BITS;
-  static constexpr uint64_t MASK = (1ull << BITS) - 1;
-  static_assert((uint64_t)(NT * TK_J) <= MASK && RowShape<NT>::ROUNDS <= 2 * PER_WORD, "fields hold a round's total");
-};
-template <int NT>
-__device__ __forceinline__ void pack_add(Packed &p, int rr, int c) {
-  using PS = PackShape<NT>;
-  if (rr < PS::PER_WORD)
-    p.w0 += (uint64_t)c << (PS::BITS * rr);
-  else
-    p.w1 += (uint64_t)c << (PS::BITS * (rr - PS::PER_WORD));
-}
-template <int NT>
-__device__ __forceinline__ int pack_get(const Packed &p, int rr) {
-  using PS = PackShape<NT>;
-  return (int)((rr < PS::PER_WORD ? p.w0 >> (PS::BITS * rr) : p.w1 >> (PS::BITS * (rr - PS::PER_WORD))) & PS::MASK);
-}
-
-// Exclusive position-order offsets of this thread's per-round counts `cnt`:
-// off[rr] = (items in earlier rounds) + (items of earlier threads in round rr).
-// Returns the block total.
-template <int NT>
-__device__ __forceinline__ int ordered_offsets(const Packed &cnt, uint64_t *sm64, int *off) {
-  uint64_t t0, t1;
-  const uint64_t e0 = block_exclusive_scan<NT>(cnt.w0, sm64, t0);
-  const uint64_t e1 = block_exclusive_scan<NT>(cnt.w1, sm64, t1);
-  const Packed ex{e0, e1}, tot{t0, t1};
-  int before = 0;
-#pragma unroll
-  for (int rr = 0; rr < RowShape<NT>::ROUNDS; ++rr) {
-    off[rr] = before + pack_get<NT>(ex, rr);
-    before += pack_get<NT>(tot, rr);
-  }
-  return before;
-}
-
-__device__ __forceinline__ void write_short(int32_t *out, int32_t *count, int q, int n, int k, int nt) {
-  for (int i = threadIdx.x; i < k; i += nt) out[i] = (i < n) ? i : -1;
-  if (threadIdx.x == 0 && count) count[q] = n;
-}
-
 // ------------------------------------------------------------------ kernels
-__global__ __launch_bounds__(256) void topk_zero_kernel(uint32_t *p, int64_t n) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0u;
+// Clears one row's first-digit histogram per block (TOPK_BINS words: 256
+// threads x two 16-byte stores).
+__global__ __launch_bounds__(256) void topk_zero_kernel(uint32_t *p) {
+  uint4 *r = reinterpret_cast<uint4 *>(p + (int64_t)blockIdx.x * TOPK_BINS);
+  static_assert(TOPK_BINS == 256 * 8, "two uint4 per thread");
+  r[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
+  r[threadIdx.x + 256] = make_uint4(0u, 0u, 0u, 0u);
 }
 
 // First-digit histogram of the rows longer than TOPK_ROW_MAX (standalone top-k).
@@ -275,113 +139,14 @@ struct SelectArgs {
   TopkWs ws;
 };
 
-// Selects row q (n <= TOPK_ROW_MAX scores) with one block of NT threads:
-// digit 1 from the indexer's histogram or from LDS atomics, digits 2 and 3 as
-// LDS histograms of the keys in the threshold bins, then the position-ordered
-// compaction.  Every thread of the block calls it (it has block barriers).
+// Selects row q (n <= TOPK_ROW_MAX scores) with one block of NT threads,
+// digit 1 from the indexer's histogram when it built one.
 template <int NT>
 __device__ void row_select(const SelectArgs &a, const int q, const int n, uint32_t *h, int *sm, uint64_t *sm64,
                            int *res) {
-  using RS = RowShape<NT>;
-  const int k = a.k;
-  const int t = threadIdx.x;
-  int32_t *out = a.idx + (int64_t)q * k;
-  if (n <= k) {
-    write_short(out, a.count, q, n, k, NT);
-    return;
-  }
-  uint32_t key[RS::PER];
-  load_keys<NT>(a.scores + (int64_t)q * a.ld, 0, (int)min((int64_t)n, a.ld), key);  // never past the row's ld
-  // Digit 1: key[31:21].
-  if (a.hist1_valid) {
-    const uint32_t *gh = a.ws.hist + (int64_t)q * TOPK_BINS;
-    for (int b = t; b < TOPK_BINS; b += NT) h[b] = gh[b];
-  } else {
-    zero_lds<NT>(h, TOPK_BINS);
-    __syncthreads();
-#pragma unroll
-    for (int rr = 0; rr < RS::ROUNDS; ++rr)
-#pragma unroll
-      for (int j = 0; j < TK_J; ++j)
-        atomicAdd(&h[key[TK_J * rr + j] >> 21], 1u);  // padding keys land in bin 0
-  }
-  __syncthreads();
-  find_rank_bin<NT, TOPK_BINS>(h, k, sm, res);
-  const uint32_t b1 = (uint32_t)res[0];
-  const int r = k - res[1];
-  __syncthreads();
-  // Digit 2: key[20:10] of the keys in bin B1.
-  zero_lds<NT>(h, TOPK_BINS);
-  __syncthreads();
-#pragma unroll
-  for (int rr = 0; rr < RS::ROUNDS; ++rr)
-#pragma unroll
-    for (int j = 0; j < TK_J; ++j) {
-      const uint32_t kk = key[TK_J * rr + j];
-      if ((kk >> 21) == b1) atomicAdd(&h[(kk >> 10) & 2047u], 1u);
-    }
-  __syncthreads();
-  find_rank_bin<NT, TOPK_BINS>(h, r, sm, res);
-  const uint32_t pre = (b1 << 11) | (uint32_t)res[0];
-  const int r2 = r - res[1];
-  __syncthreads();
-  // Digit 3: key[9:0] of the keys with key[31:10] == pre.
-  zero_lds<NT>(h, 1024);
-  __syncthreads();
-#pragma unroll
-  for (int rr = 0; rr < RS::ROUNDS; ++rr)
-#pragma unroll
-    for (int j = 0; j < TK_J; ++j) {
-      const uint32_t kk = key[TK_J * rr + j];
-      if ((kk >> 10) == pre) atomicAdd(&h[kk & 1023u], 1u);
-    }
-  __syncthreads();
-  find_rank_bin<NT, 1024>(h, r2, sm, res);
-  const uint32_t kth = (pre << 10) | (uint32_t)res[0];
-  const int ties = r2 - res[1];
-  // Emit in position order: keys > kth, and the first `ties` keys == kth.
-  Packed tc{0, 0};
-#pragma unroll
-  for (int rr = 0; rr < RS::ROUNDS; ++rr) {
-    int c = 0;
-#pragma unroll
-    for (int j = 0; j < TK_J; ++j) c += (key[TK_J * rr + j] == kth) ? 1 : 0;
-    pack_add<NT>(tc, rr, c);
-  }
-  int toff[RS::ROUNDS];
-  ordered_offsets<NT>(tc, sm64, toff);
-  Packed sc{0, 0};
-  uint32_t selbits[RS::ROUNDS];
-#pragma unroll
-  for (int rr = 0; rr < RS::ROUNDS; ++rr) {
-    int tr = toff[rr], c = 0;
-    uint32_t bits = 0;
-#pragma unroll
-    for (int j = 0; j < TK_J; ++j) {
-      const uint32_t kk = key[TK_J * rr + j];
-      const bool tie = kk == kth;
-      const bool sel = kk > kth || (tie && tr < ties);
-      tr += tie ? 1 : 0;
-      c += sel ? 1 : 0;
-      bits |= (uint32_t)sel << j;
-    }
-    selbits[rr] = bits;
-    pack_add<NT>(sc, rr, c);
-  }
-  int soff[RS::ROUNDS];
-  const int tot = ordered_offsets<NT>(sc, sm64, soff);
-#pragma unroll
-  for (int rr = 0; rr < RS::ROUNDS; ++rr) {
-    int pos = soff[rr];
-#pragma unroll
-    for (int j = 0; j < TK_J; ++j)
-      if (selbits[rr] & (1u << j)) {
-        if (pos < k) out[pos] = slot_pos<NT>(t, rr, j);
-        ++pos;
-      }
-  }
-  for (int i = tot + t; i < k; i += NT) out[i] = -1;  // defensive: tot == k
-  if (t == 0 && a.count) a.count[q] = min(tot, k);
+  select_row<NT>(a.scores + (int64_t)q * a.ld, (int)min((int64_t)n, a.ld), a.k,  // never past the row's ld
+                 a.hist1_valid ? HIST_GLOBAL : HIST_BUILD, a.ws.hist + (int64_t)q * TOPK_BINS, h, sm, sm64, res,
+                 a.idx + (int64_t)q * a.k, a.count ? a.count + q : nullptr);
 }
 
 // Three wavefronts per SIMD (at most 168 VGPRs; the 64 keys per thread take
@@ -415,6 +180,216 @@ __device__ __forceinline__ int wave_excl_small(int c, int &total) {
   }
   total = tot;
   return ex;
+}
+
+// ---------------------------------------------------------------- streaming
+// One 1024-thread block per row of up to TOPK_STREAM_MAX positions.  The
+// row's first-digit histogram (built with the scores) gives the threshold bin
+// B1 and the count above it before the block reads a score.  Wavefront w then
+// streams its 1/16 of the row, ST_D rounds of 512 scores in flight, and keeps
+// the candidates (digit 1 >= B1: the k largest and the rest of bin B1, about
+// k + |B1| keys) as (key, position) pairs in LDS, each wavefront reserving
+// its slots with one LDS atomic per round.  Digits 2 and 3 are LDS
+// histograms over the candidates; the chosen positions (and, separately,
+// the keys equal to the k-th) are marked in position bitmaps, the lowest
+// positions among the ties are kept, and block scans over the bitmap words
+// emit the positions in ascending order.  If more candidates arrive than LDS
+// holds, the digit passes re-read the row instead (same result, slower).
+constexpr int ST_THREADS = 1024;
+constexpr int ST_WAVES = ST_THREADS / WAVE;                          // 16
+constexpr int ST_ROUNDS = TOPK_STREAM_MAX / (ST_WAVES * 512);        // 16 rounds of 512 per wavefront
+constexpr int ST_D = 4;                                              // rounds in flight per wavefront
+constexpr int ST_CAP = 12288;                                        // candidates kept in LDS
+constexpr int ST_WORDS = TOPK_STREAM_MAX / 32;                       // position bitmap words
+constexpr int ST_WORDS_PER_THREAD = ST_WORDS / ST_THREADS;           // 4
+static_assert(ST_WORDS_PER_THREAD * ST_THREADS == ST_WORDS && ST_ROUNDS * ST_WAVES * 512 == TOPK_STREAM_MAX,
+              "whole rounds and bitmap words");
+
+__global__ __launch_bounds__(ST_THREADS) void topk_stream_kernel(SelectArgs a) {
+  const int q = blockIdx.x;
+  const int n = a.q_nvis[q];
+  const int k = a.k;
+  const int t = threadIdx.x;
+  __shared__ uint32_t h[TOPK_BINS];
+  __shared__ int sm[ST_WAVES];
+  __shared__ uint64_t sm64[ST_WAVES];
+  __shared__ int res[2];
+  __shared__ uint32_t ck[ST_CAP];    // candidate keys
+  __shared__ uint32_t cpos[ST_CAP];  // candidate positions
+  __shared__ uint32_t bm[ST_WORDS];  // selected positions
+  __shared__ uint32_t tbm[ST_WORDS]; // positions whose key equals the k-th
+  __shared__ int ncand;
+  int32_t *out = a.idx + (int64_t)q * k;
+  const float *row = a.scores + (int64_t)q * a.ld;
+  const uint32_t *gh = a.ws.hist + (int64_t)q * TOPK_BINS;
+  if (n <= TOPK_ROW_MAX) {  // fits the registers of the block: one-block radix select (block-uniform)
+    select_row<ST_THREADS>(row, (int)min((int64_t)n, a.ld), k, a.hist1_valid ? HIST_GLOBAL : HIST_BUILD, gh, h, sm,
+                           sm64, res, out, a.count ? a.count + q : nullptr);
+    return;
+  }
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & (WAVE - 1);
+  const int span = ((n + ST_WAVES - 1) / ST_WAVES + 511) / 512 * 512;
+  const int p0 = wave * span, p1 = min(n, p0 + span);
+  const int rounds = p1 > p0 ? (p1 - p0 + 511) / 512 : 0;  // wave-uniform
+
+  // The histogram is requested before the scores: loads complete in issue
+  // order, so the wait for it does not wait for them.
+  uint32_t hv[TOPK_BINS / ST_THREADS];
+#pragma unroll
+  for (int i = 0; i < TOPK_BINS / ST_THREADS; ++i) hv[i] = gh[t + i * ST_THREADS];
+  // Every lane issues the same loads for every round (positions past the
+  // wavefront's end read position 0 of the row), so the waits stay exact; a
+  // float4 at a position < p1 stays inside the row (ld % 4 == 0).
+  float4 f[ST_D + 1][2];
+  auto load_round = [&](const int u, float4 *dst) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int ii = p0 + 512 * u + 8 * lane + 4 * hh;
+      dst[hh] = *reinterpret_cast<const float4 *>(row + (ii < p1 ? ii : 0));
+    }
+  };
+#pragma unroll
+  for (int u = 0; u < ST_D; ++u) load_round(u, f[u]);
+#pragma unroll
+  for (int i = 0; i < TOPK_BINS / ST_THREADS; ++i) h[t + i * ST_THREADS] = hv[i];
+  if (t == 0) ncand = 0;
+  __syncthreads();
+  find_rank_bin<ST_THREADS, TOPK_BINS>(h, k, sm, res);
+  const uint32_t b1 = (uint32_t)res[0];
+  const int r = k - res[1];
+
+#pragma unroll
+  for (int u = 0; u < ST_ROUNDS; ++u) {
+    if (u + ST_D < ST_ROUNDS) load_round(u + ST_D, f[(u + ST_D) % (ST_D + 1)]);
+    if (u < rounds) {  // wave-uniform
+      const float4 *fb = f[u % (ST_D + 1)];
+      const float v[8] = {fb[0].x, fb[0].y, fb[0].z, fb[0].w, fb[1].x, fb[1].y, fb[1].z, fb[1].w};
+      const int i0 = p0 + 512 * u + 8 * lane;
+      uint32_t key[8];
+      int cnt = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        key[j] = (i0 + j < p1) ? order_key(v[j]) : 0u;  // 0: below any real key's bin
+        cnt += ((key[j] >> 21) >= b1) ? 1 : 0;
+      }
+      int tot;
+      const int ex = wave_excl_small(cnt, tot);
+      if (tot > 0) {  // wave-uniform
+        int base = 0;
+        if (lane == 0) base = atomicAdd(&ncand, tot);
+        base = __builtin_amdgcn_readfirstlane(base);
+        int pos = base + ex;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if ((key[j] >> 21) >= b1) {
+            if (pos < ST_CAP) {
+              ck[pos] = key[j];
+              cpos[pos] = (uint32_t)(i0 + j);
+            }
+            ++pos;
+          }
+      }
+    }
+  }
+  __syncthreads();
+  const int ntot = ncand;
+  const bool over = ntot > ST_CAP;  // block-uniform
+
+  // Applies f(key, position) to every candidate: from LDS, or, when LDS
+  // overflowed, to every key of the row with digit 1 >= B1, re-read.
+  auto for_each = [&](auto &&fn) {
+    if (!over) {
+      for (int i = t; i < ntot; i += ST_THREADS) fn(ck[i], cpos[i]);
+    } else {
+      for (int i = 4 * t; i < n; i += 4 * ST_THREADS) {
+        const float4 x = *reinterpret_cast<const float4 *>(row + i);
+        const float xv[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t kk = order_key(xv[e]);
+          if (i + e < n && (kk >> 21) >= b1) fn(kk, (uint32_t)(i + e));
+        }
+      }
+    }
+  };
+
+  // Digit 2: key[20:10] of the candidates in bin B1.
+  zero_lds<ST_THREADS>(h, TOPK_BINS);
+  __syncthreads();
+  for_each([&](uint32_t kk, uint32_t) {
+    if ((kk >> 21) == b1) atomicAdd(&h[(kk >> 10) & 2047u], 1u);
+  });
+  __syncthreads();
+  find_rank_bin<ST_THREADS, TOPK_BINS>(h, r, sm, res);
+  const uint32_t pre = (b1 << 11) | (uint32_t)res[0];
+  const int r2 = r - res[1];
+  __syncthreads();
+  // Digit 3: key[9:0] of the candidates with key[31:10] == pre.
+  zero_lds<ST_THREADS>(h, 1024);
+  __syncthreads();
+  for_each([&](uint32_t kk, uint32_t) {
+    if ((kk >> 10) == pre) atomicAdd(&h[kk & 1023u], 1u);
+  });
+  __syncthreads();
+  find_rank_bin<ST_THREADS, 1024>(h, r2, sm, res);
+  const uint32_t kth = (pre << 10) | (uint32_t)res[0];
+  const int ties = r2 - res[1];
+  const int tie_total = (int)h[res[0]];
+  // Mark keys above the k-th, and keys equal to it, in position bitmaps.
+#pragma unroll
+  for (int i = 0; i < ST_WORDS_PER_THREAD; ++i) {
+    bm[t * ST_WORDS_PER_THREAD + i] = 0u;
+    tbm[t * ST_WORDS_PER_THREAD + i] = 0u;
+  }
+  __syncthreads();
+  for_each([&](uint32_t kk, uint32_t p) {
+    if (kk > kth) atomicOr(&bm[p >> 5], 1u << (p & 31));
+    else if (kk == kth) atomicOr(&tbm[p >> 5], 1u << (p & 31));
+  });
+  __syncthreads();
+  // Thread t owns bitmap words [4t, 4t + 4), positions [128t, 128t + 128):
+  // thread order is position order.
+  uint32_t w[ST_WORDS_PER_THREAD];
+#pragma unroll
+  for (int i = 0; i < ST_WORDS_PER_THREAD; ++i) w[i] = tbm[t * ST_WORDS_PER_THREAD + i];
+  if (ties < tie_total) {  // block-uniform: only the `ties` lowest positions among the ties
+    int c = 0;
+#pragma unroll
+    for (int i = 0; i < ST_WORDS_PER_THREAD; ++i) c += __popc(w[i]);
+    int tt;
+    int rank = block_exclusive_scan<ST_THREADS>(c, sm, tt);
+#pragma unroll
+    for (int i = 0; i < ST_WORDS_PER_THREAD; ++i) {
+      uint32_t m = w[i], keep = 0u;
+      while (m) {
+        const uint32_t bit = m & (0u - m);
+        if (rank < ties) keep |= bit;
+        ++rank;
+        m ^= bit;
+      }
+      w[i] = keep;
+    }
+  }
+  int c = 0;
+#pragma unroll
+  for (int i = 0; i < ST_WORDS_PER_THREAD; ++i) {
+    w[i] |= bm[t * ST_WORDS_PER_THREAD + i];
+    c += __popc(w[i]);
+  }
+  int tot;
+  int pos = block_exclusive_scan<ST_THREADS>(c, sm, tot);
+#pragma unroll
+  for (int i = 0; i < ST_WORDS_PER_THREAD; ++i) {
+    uint32_t m = w[i];
+    while (m) {
+      const int b = __ffs(m) - 1;
+      if (pos < k) out[pos] = 32 * (t * ST_WORDS_PER_THREAD + i) + b;
+      ++pos;
+      m &= m - 1;
+    }
+  }
+  for (int i = tot + t; i < k; i += ST_THREADS) out[i] = -1;  // defensive: tot == k
+  if (t == 0 && a.count) a.count[q] = min(tot, k);
 }
 
 __global__ __launch_bounds__(LONG_THREADS) void topk_long_kernel(SelectArgs a) {
@@ -466,6 +441,10 @@ __global__ __launch_bounds__(LONG_THREADS) void topk_long_kernel(SelectArgs a) {
   find_rank_bin<LONG_THREADS, TOPK_BINS>(h, k, sm, res);
   const uint32_t b1 = (uint32_t)res[0];
   if (c == 0 && t == 0) a.ws.b1info[q] = make_uint2((uint32_t)res[0], (uint32_t)res[1]);
+  // h turns into this span's histogram of the second digit over its keys in
+  // bin B1 (find_rank_bin ends with a barrier: every thread is done with it).
+  zero_lds<LONG_THREADS>(h, TOPK_BINS);
+  __syncthreads();
 
   // Candidates in position order.
   uint2 *lst = a.ws.cand + (((int64_t)q * nblk + c) * TOPK_LONG_WAVES + wave) * TOPK_WAVE_SPAN;
@@ -485,148 +464,43 @@ __global__ __launch_bounds__(LONG_THREADS) void topk_long_kernel(SelectArgs a) {
     int pos = wc + wave_excl_small(cnt, tot);
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      if ((key[j] >> 21) >= b1) lst[pos++] = make_uint2(key[j], (uint32_t)(i0 + j));
+      if ((key[j] >> 21) >= b1) {
+        lst[pos++] = make_uint2(key[j], (uint32_t)(i0 + j));
+        if ((key[j] >> 21) == b1) atomicAdd(&h[(key[j] >> 10) & 2047u], 1u);
+      }
     wc += tot;
   }
   if (lane == 0) a.ws.wcnt[((int64_t)q * nblk + c) * TOPK_LONG_WAVES + wave] = (uint32_t)wc;
+  __syncthreads();
+  uint32_t *h2 = a.ws.hist2 + ((int64_t)q * nblk + c) * TOPK_BINS;
+#pragma unroll
+  for (int i = 0; i < TOPK_BINS / LONG_THREADS; ++i) h2[t + i * LONG_THREADS] = h[t + i * LONG_THREADS];
 }
 
 __global__ __launch_bounds__(LONG_THREADS) void topk_finish_kernel(SelectArgs a) {
-  const int nblk = a.ws.nblk;
   const int q = blockIdx.x;
   const int n = a.q_nvis[q];
   const int k = a.k;
-  if (n <= TOPK_ROW_MAX) return;  // topk_row_kernel
-  const int nb = (n + TOPK_LONG_SPAN - 1) / TOPK_LONG_SPAN;
+  if (n <= TOPK_ROW_MAX) return;  // selected whole by topk_long_kernel
   __shared__ uint32_t h[TOPK_BINS];
   __shared__ int sm[LONG_THREADS / WAVE];
   __shared__ int res[2];
-  __shared__ uint2 tl[TAIL_CAP];
-  __shared__ int off[TOPK_MAX_CHUNKS / 2 * TOPK_LONG_WAVES + 1];
-  const int t = threadIdx.x;
-
-  // Everything that does not depend on anything else is requested at once.
-  const uint2 bi = a.ws.b1info[q];
-  const uint32_t b1 = bi.x;
-  const int r = k - (int)bi.y;
-  const int nseg = nb * TOPK_LONG_WAVES;  // lists in position order: (block, wavefront)
-  zero_lds<LONG_THREADS>(h, TOPK_BINS);
-  const uint32_t *gw = a.ws.wcnt + (int64_t)q * nblk * TOPK_LONG_WAVES;
-  {
-    static_assert(TOPK_MAX_CHUNKS / 2 * TOPK_LONG_WAVES <= LONG_THREADS, "one list count per thread");
-    int tot;
-    const int ex = block_exclusive_scan<LONG_THREADS>(t < nseg ? (int)gw[t] : 0, sm, tot);
-    if (t < nseg) off[t] = ex;
-    if (t == 0) off[nseg] = tot;
-  }
-  __syncthreads();
-  const int ntot = off[nseg];
-  const uint2 *cq = a.ws.cand + (int64_t)q * nblk * TOPK_LONG_SPAN;
-  const bool in_lds = ntot <= TAIL_CAP;
-  // Candidate i lives in list s (off[s] <= i < off[s+1]) at index i - off[s].
-  auto locate = [&](int i) {
-    int lo = 0, hi = nseg;  // largest s with off[s] <= i
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (off[mid] <= i) lo = mid; else hi = mid;
-    }
-    return cq[(int64_t)lo * TOPK_WAVE_SPAN + (i - off[lo])];
-  };
-  if (in_lds)
-    for (int i = t; i < ntot; i += LONG_THREADS) tl[i] = locate(i);
-  __syncthreads();
-  auto get = [&](int i) { return in_lds ? tl[i] : locate(i); };
-  // Digit 2: key[20:10] of the candidates in bin B1.
-  for (int i = t; i < ntot; i += LONG_THREADS) {
-    const uint32_t kk = get(i).x;
-    if ((kk >> 21) == b1) atomicAdd(&h[(kk >> 10) & 2047u], 1u);
-  }
-  __syncthreads();
-  find_rank_bin<LONG_THREADS, TOPK_BINS>(h, r, sm, res);
-  const uint32_t pre = (b1 << 11) | (uint32_t)res[0];
-  const int r2 = r - res[1];
-  const int nbound = (int)h[res[0]];  // candidates with key[31:10] == pre
-  const int per = (ntot + LONG_THREADS - 1) / LONG_THREADS;
-  const int lo = min(ntot, per * t), hi = min(ntot, lo + per);
+  __shared__ uint32_t ck[TAIL_CAP], cpos[TAIL_CAP];
+  __shared__ int off[TOPK_MAX_LISTS + 1];
+  __shared__ int bidx[WAVE];
+  __shared__ int nb_cnt;
+  const FinishLds s{ck, cpos, TAIL_CAP, h, off, sm, res, bidx, &nb_cnt};
   int32_t *out = a.idx + (int64_t)q * k;
-  int tot;
-  if (in_lds && nbound <= WAVE) {
-    // Few candidates share the boundary prefix (the usual case): one
-    // wavefront ranks them by (key descending, position ascending) and marks
-    // the chosen r2 in place (key all ones) and the rest (key 0), so the
-    // output below is a single comparison against the prefix.
-    __shared__ int nb_cnt;
-    __shared__ int bidx[WAVE];
-    if (t == 0) nb_cnt = 0;
-    __syncthreads();
-    for (int i = t; i < ntot; i += LONG_THREADS)
-      if ((tl[i].x >> 10) == pre) bidx[atomicAdd(&nb_cnt, 1)] = i;
-    __syncthreads();
-    if (t < WAVE) {
-      const bool have = t < nbound;
-      const uint2 me = have ? tl[bidx[t]] : make_uint2(0u, 0u);
-      int rank = 0;
-      for (int j = 0; j < nbound; ++j) {
-        const uint2 o = tl[bidx[j]];
-        rank += (o.x > me.x || (o.x == me.x && o.y < me.y)) ? 1 : 0;
-      }
-      // every lane has read every boundary entry before any is overwritten
-      __builtin_amdgcn_wave_barrier();
-      if (have) tl[bidx[t]].x = rank < r2 ? 0xFFFFFFFFu : 0u;
-    }
-    __syncthreads();
-    // Output in position order: key[31:10] > pre (the marked boundary keys included).
-    int my_sel = 0;
-    for (int i = lo; i < hi; ++i) my_sel += ((tl[i].x >> 10) > pre) ? 1 : 0;
-    int pos = block_exclusive_scan<LONG_THREADS>(my_sel, sm, tot);
-    for (int i = lo; i < hi; ++i) {
-      const uint2 e = tl[i];
-      if ((e.x >> 10) > pre) {
-        if (pos < k) out[pos] = (int32_t)e.y;
-        ++pos;
-      }
-    }
-  } else {
-    __syncthreads();
-    zero_lds<LONG_THREADS>(h, 1024);
-    __syncthreads();
-    // Digit 3 over the candidates with key[31:10] == pre; contiguous runs per thread.
-    for (int i = lo; i < hi; ++i) {
-      const uint32_t kk = get(i).x;
-      if ((kk >> 10) == pre) atomicAdd(&h[kk & 1023u], 1u);
-    }
-    __syncthreads();
-    find_rank_bin<LONG_THREADS, 1024>(h, r2, sm, res);
-    const uint32_t kth = (pre << 10) | (uint32_t)res[0];
-    const int ties = r2 - res[1];
-    // Output in position order: keys > kth and the first `ties` keys == kth.
-    int my_ties = 0;
-    for (int i = lo; i < hi; ++i) my_ties += (get(i).x == kth) ? 1 : 0;
-    const int tie_rank = block_exclusive_scan<LONG_THREADS>(my_ties, sm, tot);
-    int my_sel = 0;
-    for (int i = lo, tr = tie_rank; i < hi; ++i) {
-      const uint32_t kk = get(i).x;
-      if (kk > kth || (kk == kth && tr < ties)) ++my_sel;
-      tr += (kk == kth) ? 1 : 0;
-    }
-    int pos = block_exclusive_scan<LONG_THREADS>(my_sel, sm, tot);
-    for (int i = lo, tr = tie_rank; i < hi; ++i) {
-      const uint2 e = get(i);
-      if (e.x > kth || (e.x == kth && tr < ties)) {
-        if (pos < k) out[pos] = (int32_t)e.y;
-        ++pos;
-      }
-      tr += (e.x == kth) ? 1 : 0;
-    }
-  }
-  for (int i = tot + t; i < k; i += LONG_THREADS) out[i] = -1;  // defensive: tot == k
-  if (t == 0 && a.count) a.count[q] = min(tot, k);
+  const int tot = finish_row<LONG_THREADS>(a.ws, q, n, k, s, [] {}, [&](int o, uint32_t p) {
+    if (o < k) out[o] = (int32_t)p;
+  });
+  for (int i = tot + threadIdx.x; i < k; i += LONG_THREADS) out[i] = -1;  // defensive: tot == k
+  if (threadIdx.x == 0 && a.count) a.count[q] = min(tot, k);
 }
 
 hipError_t launch_topk_init(const TopkWs &ws, int num_q, hipStream_t st) {
-  const int64_t n = (int64_t)num_q * TOPK_BINS;
-  if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(topk_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, ws.hist, n);
+  if (num_q == 0) return hipSuccess;
+  hipLaunchKernelGGL(topk_zero_kernel, dim3((unsigned)num_q), dim3(256), 0, st, ws.hist);
   return hipGetLastError();
 }
 
@@ -644,8 +518,12 @@ hipError_t launch_topk_select(const float *scores, int64_t ld, const int32_t *q_
                               hipStream_t st) {
   if (num_q == 0) return hipSuccess;
   SelectArgs a{scores, ld, q_nvis, k, hist1_valid ? 1 : 0, idx, count, ws};
-  if (ws.nblk == 0 || max_nvis <= TOPK_ROW_MAX) {  // every row fits one row block
+  if (max_nvis <= TOPK_ROW_MAX) {  // every row fits one row block
     hipLaunchKernelGGL(topk_row_kernel, dim3((unsigned)num_q), dim3(TK_THREADS), 0, st, a);
+    return hipGetLastError();
+  }
+  if (ws.nblk == 0) {  // rows up to TOPK_STREAM_MAX: one streaming block per row
+    hipLaunchKernelGGL(topk_stream_kernel, dim3((unsigned)num_q), dim3(ST_THREADS), 0, st, a);
     return hipGetLastError();
   }
   // Some row is long: the long kernel finds each long row's threshold bin and

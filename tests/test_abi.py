@@ -51,9 +51,16 @@ def test_workspace_sizes():
     L = _lib.lib()
     q = _queries(64, 131072)
     topk = L.dsa_workspace_bytes(_lib.DSA_OP_TOPK, ctypes.byref(q), 2048)
-    assert topk >= 64 * 131072 * 8  # candidate lists
+    assert topk >= 64 * 131072 * 8  # candidate lists of the two-kernel path
+    q16 = _queries(16, 131072)
+    t16 = L.dsa_workspace_bytes(_lib.DSA_OP_TOPK, ctypes.byref(q16), 2048)
+    assert 16 * 2048 * 4 <= t16 < 16 * 131072  # one streaming block per row: histograms only
     fwd = L.dsa_workspace_bytes(_lib.DSA_OP_FORWARD, ctypes.byref(q), 2048)
     assert fwd >= topk + 64 * 131072 * 4  # plus the score rows
+    q128 = _queries(128, 131072)  # from 128 rows: streaming again
+    assert L.dsa_workspace_bytes(_lib.DSA_OP_TOPK, ctypes.byref(q128), 2048) < 128 * 131072
+    q_long = _queries(64, 262144)
+    assert L.dsa_workspace_bytes(_lib.DSA_OP_TOPK, ctypes.byref(q_long), 2048) >= 64 * 262144 * 8  # candidate lists
     assert L.dsa_workspace_bytes(_lib.DSA_OP_MLA_PREFILL, ctypes.byref(q), 2048) == 0
     dec = L.dsa_workspace_bytes(_lib.DSA_OP_MLA_DECODE, ctypes.byref(q), 2048)
     assert dec >= 64 * 4 * 128 * 512 * 4  # four splits of fp32 partials

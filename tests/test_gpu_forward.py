@@ -49,3 +49,47 @@ def test_small_k():
     g = GpuInputs(wl)
     out, lse, idx = run_forward(g, k=64)
     check_queries(wl, g, out, lse, idx, range(wl.nq), k=64)
+
+
+def _fwd_ws_bytes(g, k):
+    import sparse_long_context_dsa_amd as dsa
+    return dsa.dsa_workspace_bytes(dsa.DSA_OP_FORWARD, g.queries, k)
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_prefill_where_the_indexer_selects(paged):
+    """Two 6000-token causal prefills (12000 queries): one indexer block covers
+    each query's whole history, so the indexer selects each row itself and no
+    score leaves the chip (the forward's workspace then holds no score rows).
+    Every query's positions equal the standalone top-k of the same scores
+    (dsa_topk on dsa_indexer_scores), and sampled queries match the oracle."""
+    import sparse_long_context_dsa_amd as dsa
+    banner(f"forward prefill, indexer selects, paged={paged}")
+    wl = make_custom(seq_lens=[6000, 6000], device="cuda", seed=54, prefill=True, paged=paged)
+    g = GpuInputs(wl)
+    assert _fwd_ws_bytes(g, wl.k) < wl.nq * 6000 * 4, "expected the selecting indexer (no score rows)"
+    out, lse, idx = run_forward(g)
+    ref = torch.full_like(idx, -7)
+    dsa.dsa_topk(g.queries, g.scores(), wl.k, ref)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, ref), "indexer selection differs from the standalone top-k of the same scores"
+    check_queries(wl, g, out, lse, idx, [0, 1, 2, 2047, 2048, 2049, 5999, 6000, 6001, 8048, 8049, 11999])
+
+
+@pytest.mark.parametrize("k", [2048, 64])
+def test_prefill_where_the_indexer_selects_heavy_ties(k):
+    """The same path with five distinct key rows repeated along the cache, so
+    every query's scores take five values and the selection is decided by
+    the lower-position rule among exact ties."""
+    import sparse_long_context_dsa_amd as dsa
+    banner(f"forward prefill, indexer selects, heavy ties, k={k}")
+    wl = make_custom(seq_lens=[9000], device="cuda", seed=55, prefill=True)
+    wl.k_idx.copy_(wl.k_idx[torch.arange(wl.rows, device="cuda") % 5])
+    g = GpuInputs(wl)
+    assert _fwd_ws_bytes(g, k) < wl.nq * 9000 * 4, "expected the selecting indexer (no score rows)"
+    out, lse, idx = run_forward(g, k=k)
+    ref = torch.full_like(idx, -7)
+    dsa.dsa_topk(g.queries, g.scores(), k, ref)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, ref)
+    check_queries(wl, g, out, lse, idx, [0, 63, 64, 65, 2048, 2049, 4000, 8999], k=k, near_ties=False)

@@ -116,8 +116,8 @@ def test_long_row_boundaries():
 
 
 def test_short_rows_beside_long_rows():
-    """A batch with one long row sends its short rows through the long-row
-    kernel's 1024-thread row selection: the largest short row (16384), one
+    """A batch with one long row sends its short rows through the 1024-thread
+    row selection of the long-row kernel: the largest short row (16384), one
     just above k, exactly k, a tiny one, with coarse values (many ties at the
     threshold), next to a long row."""
     banner("topk short rows beside a long row")
@@ -128,3 +128,55 @@ def test_short_rows_beside_long_rows():
     rows[0][3::11] = -0.0
     assert_same(rows, nvis, 2048, "short beside long")
     assert_same(rows, nvis, 7, "short beside long, k = 7")
+
+
+def test_many_rows_take_the_two_kernel_path():
+    """Between 33 and 127 rows up to 131072 positions go through the two-kernel
+    path (spans of 32768 per block, then one finishing block per row) instead
+    of one streaming block per row; the same adversarial rows as above:
+    integer ties, signed zeros, all equal (every key a candidate), coarse
+    normals, short rows beside long ones."""
+    banner("topk two-kernel path, 40 rows")
+    rng = np.random.default_rng(41)
+    nvis, rows = [], []
+    for j in range(40):
+        n = int(rng.choice([5, 2048, 2049, 16384, 16385, 40000, 70001, 131072]))
+        kind = j % 5
+        if kind == 0:
+            v = rng.integers(0, 6, n).astype(np.float32)
+        elif kind == 1:
+            v = rng.choice(np.array([0.0, -0.0, 1.0, -1.0, 0.5], np.float32), n)
+        elif kind == 2:
+            v = np.full(n, -2.5, np.float32)
+        elif kind == 3:
+            v = np.round(rng.standard_normal(n) * 3).astype(np.float32)
+        else:
+            v = rng.standard_normal(n).astype(np.float32)
+        nvis.append(n)
+        rows.append(v)
+    nvis[0], rows[0] = 131072, rng.standard_normal(131072).astype(np.float32)
+    assert_same(rows, nvis, 2048, "two-kernel path")
+    assert_same(rows, nvis, 3, "two-kernel path, k = 3")
+
+
+def test_many_rows_streaming_again():
+    """From 128 rows the streaming kernel is back (one block per row); 130
+    rows of mixed lengths and patterns, some long enough that every key is a
+    candidate and LDS overflows into the re-reading path."""
+    banner("topk streaming, 130 rows")
+    rng = np.random.default_rng(43)
+    nvis, rows = [], []
+    for j in range(130):
+        n = int(rng.choice([7, 2049, 16385, 30000, 99999, 131072]))
+        kind = j % 4
+        if kind == 0:
+            v = np.full(n, 0.75, np.float32)
+        elif kind == 1:
+            v = rng.choice(np.array([0.0, -0.0, 2.0, -1.0], np.float32), n)
+        elif kind == 2:
+            v = np.round(rng.standard_normal(n) * 2).astype(np.float32)
+        else:
+            v = rng.standard_normal(n).astype(np.float32)
+        nvis.append(n)
+        rows.append(v)
+    assert_same(rows, nvis, 2048, "streaming, 130 rows")
