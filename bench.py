@@ -179,20 +179,25 @@ def time_forward(wl, p, steps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    ev = dsa.HipEvents(4 * steps)
+    # Five events per step: before the first kernel, before the indexer (after
+    # the top-k's histogram clear), after the indexer, after the top-k, after
+    # the attention; the top-k stage is the clear plus the selection.
+    E = 5
+    ev = dsa.HipEvents(E * steps)
     ptr = ctypes.sizeof(ctypes.c_void_p)
     base = ctypes.addressof(ev.handles)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        step((ctypes.c_void_p * 4).from_address(base + 4 * i * ptr))
+        step((ctypes.c_void_p * E).from_address(base + E * i * ptr))
     torch.cuda.synchronize()
     wall_ev = time.perf_counter() - t0
     st = {"indexer": [], "topk": [], "mla": []}
     for i in range(steps):
-        st["indexer"].append(ev.elapsed_ms(4 * i, 4 * i + 1))
-        st["topk"].append(ev.elapsed_ms(4 * i + 1, 4 * i + 2))
-        st["mla"].append(ev.elapsed_ms(4 * i + 2, 4 * i + 3))
+        b = E * i
+        st["indexer"].append(ev.elapsed_ms(b + 1, b + 2))
+        st["topk"].append(ev.elapsed_ms(b, b + 1) + ev.elapsed_ms(b + 2, b + 3))
+        st["mla"].append(ev.elapsed_ms(b + 3, b + 4))
     ev.close()
     return wall, {k: float(np.mean(v)) for k, v in st.items()}, wall_ev
 

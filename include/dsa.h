@@ -320,11 +320,12 @@ int dsa_forward(const dsa_queries *queries, const dsa_kv_layout *layout,
                 float *lse, int32_t *idx_out, void *ws, size_t ws_bytes,
                 hipStream_t stream);
 
-/* dsa_forward, plus stage timing: when events is non-NULL, events[0..3]
+/* dsa_forward, plus stage timing: when events is non-NULL, events[0..4]
  * (created by the caller, NULL entries skipped) are recorded on `stream`
- * before the indexer, between the indexer and the top-k, between the top-k
- * and the attention, and after the attention, so that hipEventElapsedTime
- * gives each stage's device time.  Same results as dsa_forward. */
+ * before the first kernel, after the top-k's histogram clear (just before
+ * the indexer), after the indexer, after the top-k and after the attention,
+ * so that hipEventElapsedTime gives each stage's device time (the top-k's
+ * is [0, 1] + [2, 3]).  Same results as dsa_forward. */
 int dsa_forward_profiled(const dsa_queries *queries, const dsa_kv_layout *layout,
                          const uint8_t *q_fp8, const float *q_scale, const float *w,
                          const uint8_t *k_fp8, const float *k_scale, const uint16_t *q,

@@ -340,9 +340,10 @@ def dsa_indexer_backward(queries, layout, q_fp8, q_scale, w, k_fp8, k_scale, idx
 
 def dsa_forward(queries: Queries, layout: KvLayout, q_fp8, q_scale, w, k_fp8, k_scale, q, kv, k,
                 softmax_scale, out, lse=None, idx_out=None, ws=None, stream=None, events=None):
-    """events: optional ctypes array of 4 hipEvent_t handles; when given the
+    """events: optional ctypes array of 5 hipEvent_t handles; when given the
     call goes through dsa_forward_profiled, which records them between the
-    stages on the same stream."""
+    stages on the same stream (before the first kernel, before the indexer,
+    after it, after the top-k, after the attention)."""
     nq = queries.num_q
     _need(q_fp8, torch.uint8, (nq, DSA_HI, DSA_DI), "q_fp8")
     if q_scale is not None:

@@ -396,34 +396,35 @@ static int forward_impl(const dsa_queries *qr, const dsa_kv_layout *ly, const ui
     if (events && events[i] && e == hipSuccess) e = hipEventRecord(events[i], stream);
   };
   const bool sel = fwd_selects_in_indexer(qr, k);
-  if (qr->max_nvis > k && !sel) e = dsa::launch_topk_init(tw, qr->num_q, stream);
   mark(0);
+  if (qr->max_nvis > k && !sel) e = dsa::launch_topk_init(tw, qr->num_q, stream);
+  mark(1);
   if (sel) {
     // Every query's history fits one indexer block: the indexer writes the
     // positions (and the short histories' full lists); no scores, no top-k launch.
     dsa::IndexerLaunch ia{q_fp8, q_scale, w, k_fp8, k_scale, qr->q_seq, qr->q_nvis, m, nullptr, 0,
                           nullptr, k, qr->num_q, qr->max_nvis, nullptr, idx, fw.count, k};
     if (e == hipSuccess) e = dsa::launch_indexer(ia, stream);
-    mark(1);
+    mark(2);
   } else {
     if (qr->max_nvis > k && e == hipSuccess) {
       dsa::IndexerLaunch ia{q_fp8, q_scale, w, k_fp8, k_scale, qr->q_seq, qr->q_nvis, m, fw.scores, fw.ld,
                             tw.hist, k, qr->num_q, qr->max_nvis};
       e = dsa::launch_indexer(ia, stream);
     }
-    mark(1);
+    mark(2);
     if (e == hipSuccess)
       e = dsa::launch_topk_select(fw.scores, fw.ld, qr->q_nvis, k, idx, fw.count, tw, qr->num_q, qr->max_nvis,
                                   true, stream);
   }
-  mark(2);
+  mark(3);
   if (e == hipSuccess) {
     dsa::MlaLaunch ma{q, kv, idx, fw.count, qr->q_seq, qr->q_nvis, m, k, qr->num_q, softmax_scale, out, lse,
                     ly->num_rows};
     const bool decode = dsa::mla_num_splits(qr->num_q, k, true) > 1;
     e = dsa::launch_mla(ma, decode, fw.mla, stream);
   }
-  mark(3);
+  mark(4);
   return hip_status(e, "forward launch");
 }
 

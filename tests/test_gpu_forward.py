@@ -93,3 +93,43 @@ def test_prefill_where_the_indexer_selects_heavy_ties(k):
     torch.cuda.synchronize()
     assert torch.equal(idx, ref)
     check_queries(wl, g, out, lse, idx, [0, 63, 64, 65, 2048, 2049, 4000, 8999], k=k, near_ties=False)
+
+
+# ------------------------------------------------------------------ long rows
+# Batches whose longest history lies in (16384, 131072]: the forward's top-k
+# (streaming or two-kernel, from the indexer's fused histogram) must equal the
+# standalone top-k of the same scores (which builds its own histogram).
+
+def _standalone_topk(g, k):
+    import sparse_long_context_dsa_amd as dsa
+    ref = torch.full((g.wl.nq, k), -7, dtype=torch.int32, device="cuda")
+    dsa.dsa_topk(g.queries, g.scores(), k, ref)
+    torch.cuda.synchronize()
+    return ref
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_long_rows_mixed_lengths(paged):
+    """Long rows, rows of at most 16384 (one block each) and rows of at most k
+    (everything) in one batch."""
+    banner(f"forward long rows, mixed lengths, paged={paged}")
+    lens = [40000, 16384, 16385, 3000, 2048, 100000, 0, 131072, 2049, 65536]
+    wl = make_custom(seq_lens=lens, device="cuda", seed=56, paged=paged, plant=True)
+    g = GpuInputs(wl)
+    out, lse, idx = run_forward(g)
+    assert torch.equal(idx, _standalone_topk(g, wl.k)), "forward selection differs from the standalone top-k"
+    check_queries(wl, g, out, lse, idx, [0, 2, 3, 4, 6, 8, 9])
+
+
+@pytest.mark.parametrize("k", [2048, 100])
+def test_long_rows_heavy_ties(k):
+    """Five distinct key rows repeated along the cache: each score takes one of
+    five values, a fifth of the row ties in the threshold bin (more than the
+    candidate buffers hold), and ties keep the lowest positions."""
+    banner(f"forward long rows, heavy ties, k={k}")
+    wl = make_custom(seq_lens=[70000, 30000], device="cuda", seed=58)
+    wl.k_idx.copy_(wl.k_idx[torch.arange(wl.rows, device="cuda") % 5])
+    g = GpuInputs(wl)
+    out, lse, idx = run_forward(g, k=k)
+    assert torch.equal(idx, _standalone_topk(g, k))
+    check_queries(wl, g, out, lse, idx, [0, 1], k=k, near_ties=False)
