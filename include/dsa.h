@@ -312,7 +312,12 @@ int dsa_indexer_backward(const dsa_queries *queries, const dsa_kv_layout *layout
  * bypass of part 4.5 (a query with q_nvis <= k is not scored and attends to
  * every visible position).  Arguments as in the stage calls above;
  * idx_out (int32 [num_q, k]) and lse may be NULL.
- * ws : dsa_workspace_bytes(DSA_OP_FORWARD, queries, k) bytes. */
+ * ws : dsa_workspace_bytes(DSA_OP_FORWARD, queries, k) bytes.  A call leaves
+ * the workspace's top-k histograms zero, and a call whose workspace starts
+ * zero (a zero-filled buffer, or the one the previous call used) skips their
+ * clearing; any other content is detected (a histogram that does not sum to
+ * its row's length) and repaired from the scores, at some cost in time, so
+ * results never depend on it.  Calls that share a workspace must not overlap. */
 int dsa_forward(const dsa_queries *queries, const dsa_kv_layout *layout,
                 const uint8_t *q_fp8, const float *q_scale, const float *w,
                 const uint8_t *k_fp8, const float *k_scale, const uint16_t *q,
@@ -322,10 +327,10 @@ int dsa_forward(const dsa_queries *queries, const dsa_kv_layout *layout,
 
 /* dsa_forward, plus stage timing: when events is non-NULL, events[0..4]
  * (created by the caller, NULL entries skipped) are recorded on `stream`
- * before the first kernel, after the top-k's histogram clear (just before
- * the indexer), after the indexer, after the top-k and after the attention,
- * so that hipEventElapsedTime gives each stage's device time (the top-k's
- * is [0, 1] + [2, 3]).  Same results as dsa_forward. */
+ * before the first kernel, before the indexer, after the indexer, after the
+ * top-k and after the attention, so that hipEventElapsedTime gives each
+ * stage's device time (the top-k's is [0, 1] + [2, 3]; [0, 1] holds no
+ * kernel at present).  Same results as dsa_forward. */
 int dsa_forward_profiled(const dsa_queries *queries, const dsa_kv_layout *layout,
                          const uint8_t *q_fp8, const float *q_scale, const float *w,
                          const uint8_t *k_fp8, const float *k_scale, const uint16_t *q,

@@ -119,10 +119,12 @@ def dsa_workspace_bytes(op: int, queries: Queries, k: int) -> int:
 
 
 def workspace(op: int, queries: Queries, k: int, device="cuda") -> Optional[torch.Tensor]:
-    """A byte tensor of dsa_workspace_bytes(op, ...) (torch's allocator returns
-    blocks aligned to at least 256 bytes)."""
+    """A zero-filled byte tensor of dsa_workspace_bytes(op, ...) (torch's
+    allocator returns blocks aligned to at least 256 bytes).  Zero is the
+    state dsa_forward leaves it in, so reusing it across calls is the fast
+    path."""
     n = dsa_workspace_bytes(op, queries, k)
-    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)
+    return torch.zeros(max(n, 1), dtype=torch.uint8, device=device)
 
 
 def dsa_quantize_fp8(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, stream=None):

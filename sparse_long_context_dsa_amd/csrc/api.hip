@@ -396,8 +396,10 @@ static int forward_impl(const dsa_queries *qr, const dsa_kv_layout *ly, const ui
     if (events && events[i] && e == hipSuccess) e = hipEventRecord(events[i], stream);
   };
   const bool sel = fwd_selects_in_indexer(qr, k);
+  // No clear of the first-digit histograms: the top-k kernels leave them zero
+  // for the next call, and a histogram that does not sum to its row's length
+  // (a workspace that held other data) is rebuilt from the scores.
   mark(0);
-  if (qr->max_nvis > k && !sel) e = dsa::launch_topk_init(tw, qr->num_q, stream);
   mark(1);
   if (sel) {
     // Every query's history fits one indexer block: the indexer writes the

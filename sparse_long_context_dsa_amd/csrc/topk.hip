@@ -205,6 +205,23 @@ constexpr int ST_WORDS_PER_THREAD = ST_WORDS / ST_THREADS;           // 4
 static_assert(ST_WORDS_PER_THREAD * ST_THREADS == ST_WORDS && ST_ROUNDS * ST_WAVES * 512 == TOPK_STREAM_MAX,
               "whole rounds and bitmap words");
 
+// The first-digit histogram of row[0 .. n) built in LDS with one pass over
+// the scores: used when the histogram from the indexer does not sum to n (the
+// workspace held other data before the call).
+template <int NT>
+__device__ void rebuild_first_digit(const float *row, const int n, uint32_t *h) {
+  __syncthreads();
+  zero_lds<NT>(h, TOPK_BINS);
+  __syncthreads();
+  for (int i = 4 * (int)threadIdx.x; i < n; i += 4 * NT) {  // i + 3 < ld: ld is a multiple of 4
+    const float4 x = *reinterpret_cast<const float4 *>(row + i);
+    const float xv[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (i + e < n) atomicAdd(&h[order_key(xv[e]) >> 21], 1u);
+  }
+}
+
 __global__ __launch_bounds__(ST_THREADS) void topk_stream_kernel(SelectArgs a) {
   const int q = blockIdx.x;
   const int n = a.q_nvis[q];
@@ -221,7 +238,7 @@ __global__ __launch_bounds__(ST_THREADS) void topk_stream_kernel(SelectArgs a) {
   __shared__ int ncand;
   int32_t *out = a.idx + (int64_t)q * k;
   const float *row = a.scores + (int64_t)q * a.ld;
-  const uint32_t *gh = a.ws.hist + (int64_t)q * TOPK_BINS;
+  uint32_t *gh = a.ws.hist + (int64_t)q * TOPK_BINS;
   if (n <= TOPK_ROW_MAX) {  // fits the registers of the block: one-block radix select (block-uniform)
     select_row<ST_THREADS>(row, (int)min((int64_t)n, a.ld), k, a.hist1_valid ? HIST_GLOBAL : HIST_BUILD, gh, h, sm,
                            sm64, res, out, a.count ? a.count + q : nullptr);
@@ -237,6 +254,8 @@ __global__ __launch_bounds__(ST_THREADS) void topk_stream_kernel(SelectArgs a) {
   uint32_t hv[TOPK_BINS / ST_THREADS];
 #pragma unroll
   for (int i = 0; i < TOPK_BINS / ST_THREADS; ++i) hv[i] = gh[t + i * ST_THREADS];
+#pragma unroll
+  for (int i = 0; i < TOPK_BINS / ST_THREADS; ++i) gh[t + i * ST_THREADS] = 0u;  // cleared for the next call
   // Every lane issues the same loads for every round (positions past the
   // wavefront's end read position 0 of the row), so the waits stay exact; a
   // float4 at a position < p1 stays inside the row (ld % 4 == 0).
@@ -250,9 +269,16 @@ __global__ __launch_bounds__(ST_THREADS) void topk_stream_kernel(SelectArgs a) {
   };
 #pragma unroll
   for (int u = 0; u < ST_D; ++u) load_round(u, f[u]);
+  int hsum = 0;
 #pragma unroll
-  for (int i = 0; i < TOPK_BINS / ST_THREADS; ++i) h[t + i * ST_THREADS] = hv[i];
+  for (int i = 0; i < TOPK_BINS / ST_THREADS; ++i) {
+    h[t + i * ST_THREADS] = hv[i];
+    hsum += (int)hv[i];
+  }
   if (t == 0) ncand = 0;
+  int htot;
+  block_exclusive_scan<ST_THREADS>(hsum, sm, htot);
+  if (htot != n) rebuild_first_digit<ST_THREADS>(row, n, h);  // block-uniform: not only this call's counts
   __syncthreads();
   find_rank_bin<ST_THREADS, TOPK_BINS>(h, k, sm, res);
   const uint32_t b1 = (uint32_t)res[0];
@@ -435,8 +461,17 @@ __global__ __launch_bounds__(LONG_THREADS) void topk_long_kernel(SelectArgs a) {
 
   // Threshold bin B1 of the first digit and the count above it, computed by
   // every block of the row alike; the first block publishes it for the finish.
+  // A histogram that does not sum to n (the workspace held other data) is
+  // rebuilt by every block of the row from the whole row, alike.
+  int hsum = 0;
 #pragma unroll
-  for (int i = 0; i < TOPK_BINS / LONG_THREADS; ++i) h[t + i * LONG_THREADS] = hv[i];
+  for (int i = 0; i < TOPK_BINS / LONG_THREADS; ++i) {
+    h[t + i * LONG_THREADS] = hv[i];
+    hsum += (int)hv[i];
+  }
+  int htot;
+  block_exclusive_scan<LONG_THREADS>(hsum, sm, htot);
+  if (htot != n) rebuild_first_digit<LONG_THREADS>(row, n, h);  // block-uniform
   __syncthreads();
   find_rank_bin<LONG_THREADS, TOPK_BINS>(h, k, sm, res);
   const uint32_t b1 = (uint32_t)res[0];
@@ -490,6 +525,9 @@ __global__ __launch_bounds__(LONG_THREADS) void topk_finish_kernel(SelectArgs a)
   __shared__ int bidx[WAVE];
   __shared__ int nb_cnt;
   const FinishLds s{ck, cpos, TAIL_CAP, h, off, sm, res, bidx, &nb_cnt};
+  // Every block of the long kernel has read this row's first-digit histogram:
+  // clear it for the next call.
+  for (int b = threadIdx.x; b < TOPK_BINS; b += LONG_THREADS) a.ws.hist[(int64_t)q * TOPK_BINS + b] = 0u;
   int32_t *out = a.idx + (int64_t)q * k;
   const int tot = finish_row<LONG_THREADS>(a.ws, q, n, k, s, [] {}, [&](int o, uint32_t p) {
     if (o < k) out[o] = (int32_t)p;

@@ -175,9 +175,12 @@ enum HistSource { HIST_BUILD = 0, HIST_GLOBAL = 1, HIST_LDS = 2 };
 // LDS atomics, copied from `gh` in global memory, or already in `h`), digits 2
 // and 3 as LDS histograms of the keys in the threshold bins, then the
 // position-ordered compaction into out[0 .. k) and *count_out (if non-null).
-// Every thread of the block calls it (it has block barriers, for LDS only).
+// A histogram from `gh` is left cleared for the next call, and checked: if its
+// bins do not sum to n (it held more than this call's counts), digit 1 is
+// built from the keys instead.  Every thread of the block calls it (it has
+// block barriers, for LDS only).
 template <int NT>
-__device__ void select_row(const float *row, const int n, const int k, const int hist_src, const uint32_t *gh,
+__device__ void select_row(const float *row, const int n, const int k, const int hist_src, uint32_t *gh,
                            uint32_t *h, int *sm, uint64_t *sm64, int *res, int32_t *out, int32_t *count_out) {
   using RS = RowShape<NT>;
   const int t = threadIdx.x;
@@ -189,9 +192,20 @@ __device__ void select_row(const float *row, const int n, const int k, const int
   uint32_t key[RS::PER];
   load_keys<NT>(row, 0, n, key);
   // Digit 1: key[31:21].
+  bool build = hist_src == HIST_BUILD;
   if (hist_src == HIST_GLOBAL) {
-    for (int b = t; b < TOPK_BINS; b += NT) h[b] = gh[b];
-  } else if (hist_src == HIST_BUILD) {
+    int local = 0;
+    for (int b = t; b < TOPK_BINS; b += NT) {
+      const uint32_t v = gh[b];
+      h[b] = v;
+      local += (int)v;
+      gh[b] = 0u;  // each thread clears the bins it read
+    }
+    int tot;
+    block_exclusive_scan<NT>(local, sm, tot);
+    build = tot != n;  // block-uniform
+  }
+  if (build) {
     zero_lds<NT>(h, TOPK_BINS);
     lds_barrier();
 #pragma unroll

@@ -133,3 +133,36 @@ def test_long_rows_heavy_ties(k):
     out, lse, idx = run_forward(g, k=k)
     assert torch.equal(idx, _standalone_topk(g, k))
     check_queries(wl, g, out, lse, idx, [0, 1], k=k, near_ties=False)
+
+
+# ------------------------------------------------------------------ workspace state
+@pytest.mark.parametrize("lens", [[9000, 12000, 5000], [40000] * 16, [131072] * 8 + [20000] * 56],
+                         ids=["row-blocks", "streaming", "two-kernel"])
+def test_forward_workspace_contents_do_not_matter(lens):
+    """The forward leaves its top-k histograms zero in the workspace and does not
+    clear them at the start of a call.  A workspace that holds other data (here
+    0xA5 bytes) must give the same result, the histograms being checked against
+    their rows' lengths and rebuilt, and must be left clean for the next call."""
+    import sparse_long_context_dsa_amd as dsa
+    banner(f"forward workspace contents, {len(lens)} rows up to {max(lens)}")
+    wl = make_custom(seq_lens=lens, device="cuda", seed=59)
+    g = GpuInputs(wl)
+    k = wl.k
+
+    def fwd(ws):
+        out = torch.full((wl.nq, 128, 512), float("nan"), dtype=torch.float32, device="cuda")
+        lse = torch.full((wl.nq, 128), float("nan"), dtype=torch.float32, device="cuda")
+        idx = torch.full((wl.nq, k), -7, dtype=torch.int32, device="cuda")
+        dsa.dsa_forward(g.queries, g.layout, g.q8, g.qs, wl.w, g.k8, g.ks, wl.q_mla, wl.kv, k, wl.softmax_scale,
+                        out, lse, idx, ws=ws)
+        torch.cuda.synchronize()
+        return out, lse, idx
+
+    ws = dsa.workspace(dsa.DSA_OP_FORWARD, g.queries, k)
+    runs = [fwd(ws), fwd(ws)]
+    ws.fill_(0xA5)
+    runs += [fwd(ws), fwd(ws)]
+    ref = _standalone_topk(g, k)
+    for i, (out, lse, idx) in enumerate(runs):
+        assert torch.equal(idx, ref), f"run {i}: selection differs from the standalone top-k"
+        assert torch.equal(out, runs[0][0]) and torch.equal(lse, runs[0][1]), f"run {i}: output differs"
