@@ -71,7 +71,7 @@ constexpr int TOPK_WAVE_SPAN = 2048;   // positions per wavefront (4 rounds of 5
 constexpr int TOPK_LONG_SPAN = TOPK_LONG_WAVES * TOPK_WAVE_SPAN;  // 32768 positions per block
 constexpr int TOPK_STREAM_MAX = 131072;  // rows up to this length: one streaming block per row
 struct TopkWs {
-  uint32_t *hist;     // [num_q, TOPK_BINS] first-digit histogram (cleared each call)
+  uint32_t *hist;     // [num_q, TOPK_BINS] first-digit histogram (zero between calls: readers clear it)
   uint2 *b1info;      // [num_q] long rows: (first-digit threshold bin B1, keys above B1)
   uint32_t *wcnt;     // [num_q, nblk, TOPK_LONG_WAVES] candidates per wavefront
   uint2 *cand;        // [num_q, nblk, TOPK_LONG_WAVES, TOPK_WAVE_SPAN] (key, position)

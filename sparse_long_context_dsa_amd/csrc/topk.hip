@@ -81,7 +81,7 @@ TopkWs topk_ws_carve(void *ws, int num_q, int max_nvis) {
   w.nchunks = topk_nchunks(max_nvis);
   w.nblk = topk_nblk(num_q, max_nvis);
   uint8_t *p = static_cast<uint8_t *>(ws);
-  w.hist = reinterpret_cast<uint32_t *>(p);  // [nq, 2048] first digit (cleared each call)
+  w.hist = reinterpret_cast<uint32_t *>(p);  // [nq, 2048] first digit (left zero by its readers)
   p += align256(nq * TOPK_BINS * 4);
   w.b1info = reinterpret_cast<uint2 *>(p);   // [nq] written before it is read
   p += align256(nq * sizeof(uint2));
