@@ -106,6 +106,11 @@ struct MlaLaunch {
   bool dense;            // every visible position, no idx (k = the longest history)
 };
 int mla_num_splits(int num_q, int k, bool decode);
+// Whether a decode batch splits each query's heads over four workgroups
+// (mla_hg_kernel: no partials, no combine) instead of its rows (mla_kernel,
+// then the combine of the splits' partials).
+bool mla_head_groups(int num_q, int k, bool decode, bool dense);
+hipError_t launch_mla_hg(const MlaLaunch &a, float scale_log2, bool wide, hipStream_t st);
 // Row splits of the dense mode: the time model, with at most 2080 tiles of 32
 // rows per workgroup (its per-tile row table lives in LDS).
 int mla_dense_splits(int num_q, int max_nvis);

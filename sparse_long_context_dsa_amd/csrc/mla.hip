@@ -40,8 +40,6 @@
 namespace dsa {
 
 constexpr int NBUF = 3;                              // tiles in flight
-constexpr int MLA_MAX_ROWS = 2048;                   // rows per block (k <= 2048)
-constexpr float RESCALE_LOG2 = 8.0f;                 // lazy-rescale threshold (log2 units)
 
 struct MlaKernelArgs {
   MlaLaunch a;
@@ -52,53 +50,6 @@ struct MlaKernelArgs {
   float *part_lse;  // [num_q, nsplit, 128]
   int dense;        // prow holds the base row of each 32-row tile of positions
 };
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-// Two floats -> two bf16 (round to nearest even) in one word, lo in the low half.
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  const f32x2_t v = {lo, hi};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
-}
-
-// Scales one accumulator register in place.  The accumulators live in AGPRs,
-// which VALU instructions cannot use as operands; the explicit read / multiply /
-// write keeps them there instead of moving all of O into VGPRs.
-__device__ __forceinline__ void scale_acc(float &x, float s) {
-  float tmp;
-  asm volatile(
-      "v_accvgpr_read_b32 %1, %0\n\t"
-      "s_nop 1\n\t"
-      "v_mul_f32 %1, %1, %2\n\t"
-      "v_accvgpr_write_b32 %0, %1\n\t"
-      "s_nop 1"
-      : "+a"(x), "=&v"(tmp)
-      : "v"(s));
-}
-
-// One accumulator register times s, as a VGPR value (the AGPR is unchanged).
-__device__ __forceinline__ float read_scaled(const float &x, float s) {
-  float r;
-  asm("v_accvgpr_read_b32 %0, %1\n\t"
-      "s_nop 1\n\t"
-      "v_mul_f32 %0, %0, %2"
-      : "=&v"(r)
-      : "a"(x), "v"(s));
-  return r;
-}
-
-// Values of the 16 heads whose O rows this lane holds (heads 8i + 4g + j),
-// from a 32-entry per-head array in LDS.
-__device__ __forceinline__ void read_head_values(const float *x, int g, float *v) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float4 f = *reinterpret_cast<const float4 *>(&x[8 * i + 4 * g]);
-    v[4 * i + 0] = f.x;
-    v[4 * i + 1] = f.y;
-    v[4 * i + 2] = f.z;
-    v[4 * i + 3] = f.w;
-  }
-}
 
 template <bool WIDE, bool PIPE>
 __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
@@ -653,6 +604,13 @@ int mla_num_splits(int num_q, int k, bool decode) {
   return best_ns;
 }
 
+// Head groups where the row split would use three or more splits and the
+// four workgroups of every query fit one round on the chip (48 to 64
+// queries).
+bool mla_head_groups(int num_q, int k, bool decode, bool dense) {
+  return decode && !dense && num_q >= 48 && num_q <= 64 && mla_num_splits(num_q, k, true) >= 3;
+}
+
 static int rows_per_split(int k, int nsplit) {
   int r = (k + nsplit - 1) / nsplit;
   return (r + MLA_T - 1) / MLA_T * MLA_T;
@@ -666,6 +624,7 @@ int mla_dense_splits(int num_q, int max_nvis) {
 }
 
 size_t mla_ws_bytes(int num_q, int k, bool decode, bool dense) {
+  if (mla_head_groups(num_q, k, decode, dense)) return 0;  // no partials
   const int ns = dense ? mla_dense_splits(num_q, k) : mla_num_splits(num_q, k, decode);
   if (ns <= 1) return 0;
   return (size_t)num_q * ns * 128 * (512 + 1) * sizeof(float) + 256;
@@ -673,6 +632,9 @@ size_t mla_ws_bytes(int num_q, int k, bool decode, bool dense) {
 
 hipError_t launch_mla(const MlaLaunch &a, bool decode, void *ws, hipStream_t st) {
   if (a.num_q == 0) return hipSuccess;
+  // Offsets from the descriptor base stay below 4 GiB unless a paged pool is that large.
+  const bool wide = a.map.block_shift >= 0 && a.num_rows * (int64_t)ROW_BYTES >= 0xFFFFF000ll - ROW_BYTES;
+  if (mla_head_groups(a.num_q, a.k, decode, a.dense)) return launch_mla_hg(a, a.softmax_scale * LOG2E, wide, st);
   MlaKernelArgs p;
   p.a = a;
   p.nsplit = a.dense ? mla_dense_splits(a.num_q, a.k) : mla_num_splits(a.num_q, a.k, decode);
@@ -685,8 +647,6 @@ hipError_t launch_mla(const MlaLaunch &a, bool decode, void *ws, hipStream_t st)
     p.part_o = static_cast<float *>(ws);
     p.part_lse = p.part_o + (size_t)a.num_q * p.nsplit * 128 * 512;
   }
-  // Offsets from the descriptor base stay below 4 GiB unless a paged pool is that large.
-  const bool wide = a.map.block_shift >= 0 && a.num_rows * (int64_t)ROW_BYTES >= 0xFFFFF000ll - ROW_BYTES;
   const int64_t nq8 = (a.num_q + 7) / 8 * 8;  // split blocks are grouped by XCD
   const dim3 grid((unsigned)(p.nsplit == 1 ? (int64_t)a.num_q : nq8 * p.nsplit));
   // Without splits (prefill) the pipelined schedule; with them (decode) the

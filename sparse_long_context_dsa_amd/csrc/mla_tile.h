@@ -116,6 +116,56 @@ __device__ __forceinline__ void issue_tile(const __amdgpu_buffer_rsrc_t rs, cons
   for (int i = 0; i < LOADS_PER_WAVE; ++i) issue_part<WIDE>(rs, kv, brow, row, buf, wave, lane, i);
 }
 
+constexpr int MLA_MAX_ROWS = 2048;                   // selected rows per query (k <= 2048)
+constexpr float RESCALE_LOG2 = 8.0f;                 // lazy-rescale threshold (log2 units)
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+// Two floats -> two bf16 (round to nearest even) in one word, lo in the low half.
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
+
+// Scales one accumulator register in place.  The accumulators live in AGPRs,
+// which VALU instructions cannot use as operands; the explicit read / multiply /
+// write keeps them there instead of moving all of O into VGPRs.
+__device__ __forceinline__ void scale_acc(float &x, float s) {
+  float tmp;
+  asm volatile(
+      "v_accvgpr_read_b32 %1, %0\n\t"
+      "s_nop 1\n\t"
+      "v_mul_f32 %1, %1, %2\n\t"
+      "v_accvgpr_write_b32 %0, %1\n\t"
+      "s_nop 1"
+      : "+a"(x), "=&v"(tmp)
+      : "v"(s));
+}
+
+// One accumulator register times s, as a VGPR value (the AGPR is unchanged).
+__device__ __forceinline__ float read_scaled(const float &x, float s) {
+  float r;
+  asm("v_accvgpr_read_b32 %0, %1\n\t"
+      "s_nop 1\n\t"
+      "v_mul_f32 %0, %0, %2"
+      : "=&v"(r)
+      : "a"(x), "v"(s));
+  return r;
+}
+
+// Values of the 16 heads whose O rows this lane holds (heads 8i + 4g + j),
+// from a 32-entry per-head array in LDS.
+__device__ __forceinline__ void read_head_values(const float *x, int g, float *v) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float4 f = *reinterpret_cast<const float4 *>(&x[8 * i + 4 * g]);
+    v[4 * i + 0] = f.x;
+    v[4 * i + 1] = f.y;
+    v[4 * i + 2] = f.z;
+    v[4 * i + 3] = f.w;
+  }
+}
+
 // max(a, b, c) in one instruction.  fmaxf would add a canonicalising
 // instruction per operand for values the compiler cannot see (accumulators
 // written by inline asm); the scores are never signalling NaNs.

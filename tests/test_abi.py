@@ -62,8 +62,10 @@ def test_workspace_sizes():
     q_long = _queries(64, 262144)
     assert L.dsa_workspace_bytes(_lib.DSA_OP_TOPK, ctypes.byref(q_long), 2048) >= 64 * 262144 * 8  # candidate lists
     assert L.dsa_workspace_bytes(_lib.DSA_OP_MLA_PREFILL, ctypes.byref(q), 2048) == 0
-    dec = L.dsa_workspace_bytes(_lib.DSA_OP_MLA_DECODE, ctypes.byref(q), 2048)
-    assert dec >= 64 * 4 * 128 * 512 * 4  # four splits of fp32 partials
+    dec16 = L.dsa_workspace_bytes(_lib.DSA_OP_MLA_DECODE, ctypes.byref(q16), 2048)
+    assert dec16 >= 16 * 8 * 128 * 512 * 4  # eight row splits of fp32 partials
+    # 64 queries split heads, not rows: no partials
+    assert L.dsa_workspace_bytes(_lib.DSA_OP_MLA_DECODE, ctypes.byref(q), 2048) == 0
     assert L.dsa_workspace_bytes(_lib.DSA_OP_TOPK, ctypes.byref(q), 0) == ctypes.c_size_t(-1).value
     assert L.dsa_workspace_bytes(77, ctypes.byref(q), 16) == ctypes.c_size_t(-1).value
 

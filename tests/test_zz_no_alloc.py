@@ -46,7 +46,7 @@ def _both(wl, k, seed):
 def test_noalloc_matches_workspace_call_twice_second_smaller():
     k = 2048
     ws_need = []
-    for nq, seed in ((64, 401), (16, 402)):  # 4 splits (64.1 MiB of partials), then 8 splits (32.1 MiB)
+    for nq, seed in ((80, 401), (16, 402)):  # 3 splits (60.1 MiB of partials), then 8 splits (32.1 MiB)
         banner(f"noalloc decode: {nq} queries x 4096, k={k}")
         wl = make_custom(seq_lens=[4096] * nq, device="cuda", seed=seed)
         q = dsa.Queries(wl.q_seq, wl.q_nvis, wl.max_nvis)
@@ -61,6 +61,21 @@ def test_noalloc_matches_workspace_call_twice_second_smaller():
             o_ref, l_ref = ov.mla(i, idx[i])
             check_out(o_na[i], o_ref, l_na[i], l_ref, f"noalloc q{i}")
     assert ws_need[1] < ws_need[0]
+
+
+def test_noalloc_head_group_batch_needs_no_scratch():
+    """64 queries split their heads instead of their rows: no partials, so the
+    entry point uses no scratch, and its outputs equal the workspace call's."""
+    k = 2048
+    banner("noalloc decode: 64 queries x 4096 (head groups, no partials)")
+    wl = make_custom(seq_lens=[4096] * 64, device="cuda", seed=404)
+    q = dsa.Queries(wl.q_seq, wl.q_nvis, wl.max_nvis)
+    assert dsa.dsa_workspace_bytes(dsa.DSA_OP_MLA_DECODE, q, k) == 0
+    idx, ((o_na, l_na), (o_ws, l_ws)) = _both(wl, k, 404)
+    assert (o_na.view(np.uint32) == o_ws.view(np.uint32)).all()
+    assert (l_na.view(np.uint32) == l_ws.view(np.uint32)).all()
+    o_ref, l_ref = OracleView(wl).mla(63, idx[63])
+    check_out(o_na[63], o_ref, l_na[63], l_ref, "noalloc head groups q63")
 
 
 def test_noalloc_rejects_partials_beyond_the_scratch():
