@@ -106,11 +106,14 @@ struct MlaLaunch {
   bool dense;            // every visible position, no idx (k = the longest history)
 };
 int mla_num_splits(int num_q, int k, bool decode);
-// Whether a decode batch splits each query's heads over four workgroups
-// (mla_hg_kernel: no partials, no combine) instead of its rows (mla_kernel,
-// then the combine of the splits' partials).
-bool mla_head_groups(int num_q, int k, bool decode, bool dense);
-hipError_t launch_mla_hg(const MlaLaunch &a, float scale_log2, bool wide, hipStream_t st);
+// Decode batches of up to 64 queries split each query's heads over four
+// workgroups, and its rows over mla_hg_splits() of them each (mla_hg_kernel;
+// with one split no partials and no combine); 0 selects the row-split kernel
+// (mla_kernel over all 128 heads, then the combine of the splits' partials).
+int mla_hg_splits(int num_q, int k, bool decode, bool dense);
+int mla_hg_rows_per_split(int k, int nsplit);
+hipError_t launch_mla_hg(const MlaLaunch &a, float scale_log2, bool wide, int nsplit, float *part_o,
+                         float *part_lse, hipStream_t st);
 // Row splits of the dense mode: the time model, with at most 2080 tiles of 32
 // rows per workgroup (its per-tile row table lives in LDS).
 int mla_dense_splits(int num_q, int max_nvis);

@@ -604,13 +604,6 @@ int mla_num_splits(int num_q, int k, bool decode) {
   return best_ns;
 }
 
-// Head groups where the row split would use three or more splits and the
-// four workgroups of every query fit one round on the chip (48 to 64
-// queries).
-bool mla_head_groups(int num_q, int k, bool decode, bool dense) {
-  return decode && !dense && num_q >= 48 && num_q <= 64 && mla_num_splits(num_q, k, true) >= 3;
-}
-
 static int rows_per_split(int k, int nsplit) {
   int r = (k + nsplit - 1) / nsplit;
   return (r + MLA_T - 1) / MLA_T * MLA_T;
@@ -624,7 +617,9 @@ int mla_dense_splits(int num_q, int max_nvis) {
 }
 
 size_t mla_ws_bytes(int num_q, int k, bool decode, bool dense) {
-  if (mla_head_groups(num_q, k, decode, dense)) return 0;  // no partials
+  const int hs = mla_hg_splits(num_q, k, decode, dense);
+  if (hs == 1) return 0;  // head groups alone: no partials
+  if (hs > 1) return (size_t)num_q * hs * 128 * (512 + 1) * sizeof(float) + 256;
   const int ns = dense ? mla_dense_splits(num_q, k) : mla_num_splits(num_q, k, decode);
   if (ns <= 1) return 0;
   return (size_t)num_q * ns * 128 * (512 + 1) * sizeof(float) + 256;
@@ -634,10 +629,10 @@ hipError_t launch_mla(const MlaLaunch &a, bool decode, void *ws, hipStream_t st)
   if (a.num_q == 0) return hipSuccess;
   // Offsets from the descriptor base stay below 4 GiB unless a paged pool is that large.
   const bool wide = a.map.block_shift >= 0 && a.num_rows * (int64_t)ROW_BYTES >= 0xFFFFF000ll - ROW_BYTES;
-  if (mla_head_groups(a.num_q, a.k, decode, a.dense)) return launch_mla_hg(a, a.softmax_scale * LOG2E, wide, st);
+  const int hs = mla_hg_splits(a.num_q, a.k, decode, a.dense);
   MlaKernelArgs p;
   p.a = a;
-  p.nsplit = a.dense ? mla_dense_splits(a.num_q, a.k) : mla_num_splits(a.num_q, a.k, decode);
+  p.nsplit = hs > 0 ? hs : a.dense ? mla_dense_splits(a.num_q, a.k) : mla_num_splits(a.num_q, a.k, decode);
   p.dense = a.dense ? 1 : 0;
   p.rows_per_split = rows_per_split(a.k, p.nsplit);
   p.scale_log2 = a.softmax_scale * LOG2E;
@@ -651,7 +646,10 @@ hipError_t launch_mla(const MlaLaunch &a, bool decode, void *ws, hipStream_t st)
   const dim3 grid((unsigned)(p.nsplit == 1 ? (int64_t)a.num_q : nq8 * p.nsplit));
   // Without splits (prefill) the pipelined schedule; with them (decode) the
   // in-order one, whose gathers run two tiles ahead.
-  if (p.nsplit == 1) {
+  if (hs > 0) {
+    const hipError_t e = launch_mla_hg(a, p.scale_log2, wide, hs, p.part_o, p.part_lse, st);
+    if (e != hipSuccess) return e;
+  } else if (p.nsplit == 1) {
     if (wide)
       hipLaunchKernelGGL((mla_kernel<true, true>), grid, dim3(MLA_THREADS), 0, st, p);
     else

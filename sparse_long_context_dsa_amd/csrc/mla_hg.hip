@@ -5,15 +5,17 @@
 // shared latent row of each selected position; page "DeepSeekV3.2之DSA", part
 // 5.1: softmax(q . [c_kv; k_pe]^T) . c_kv, value = dims 0..511 of the row),
 // organised for a decode batch with too few queries to fill the chip with one
-// workgroup each.  Instead of splitting a query's selected rows over several
-// workgroups, whose fp32 partial outputs then make a round trip through memory
-// to a combine pass, its 128 heads are split into four groups of 32: each
-// workgroup attends over the whole selection for its 32 heads and writes final
-// outputs.  The four workgroups of a query run on one XCD at the same time
-// (block b runs on XCD b % 8), so a gathered row is read from HBM once and
-// from that XCD's L2 by the other three.  Each CU thus takes in all 2.36 MB of
-// its query's rows; the gather reads every 128-byte line of a row with eight
-// consecutive lanes, the form a CU serves at over 100 GB/s (lanes spread over
+// workgroup each.  A query's 128 heads are split into four groups of 32, and
+// for small batches (up to 32 queries) its selected rows into S splits as
+// well: 4 S workgroups per query.  With S = 1 each workgroup attends over the
+// whole selection for its 32 heads and writes final outputs, so the fp32
+// partials of a row split and their round trip through memory to a combine
+// pass are gone; with S > 1 the splits write (O / l, lse) partials, a quarter
+// of what as many row splits over all heads would, that mla_combine_kernel
+// merges.  The four head groups of a (query, split) run on one XCD at the same
+// time, so a gathered row is read from HBM once and from that XCD's L2 by the
+// other three.  Each CU thus takes in all the 1152-byte rows of its split; the
+// gather reads every 128-byte line of a row with eight consecutive lanes, the form a CU serves at over 100 GB/s (lanes spread over
 // different rows get about a third of that).
 //
 // Inside a workgroup the four wavefronts take the 16-row tiles in turn (tile j
@@ -48,6 +50,10 @@ static_assert(2 * HG_OREGION <= MLA_WAVES * HG_TILE_BYTES, "two merge regions pe
 struct MlaHgArgs {
   MlaLaunch a;
   float scale_log2;
+  int nsplit;          // row splits S per head group
+  int rows_per_split;  // a multiple of HG_T (all k rows when S = 1)
+  float *part_o;       // [num_q, S, 128, 512] (S > 1)
+  float *part_lse;     // [num_q, S, 128]
 };
 
 // Tile layout in LDS: 18 blocks of 1 KiB.  Block lc + 9 rg holds the 128-byte
@@ -95,9 +101,12 @@ __device__ __forceinline__ void mfma16_drain(v4f &a, v4f &b) {
 template <bool WIDE>
 __global__ __launch_bounds__(MLA_THREADS, 1) void mla_hg_kernel(MlaHgArgs p) {
   const MlaLaunch &a = p.a;
+  // Unit u = (query, split) runs its four head groups on XCD u % 8 (block b
+  // runs on XCD b % 8), where they share the gathered rows in L2.
   const int y = blockIdx.x >> 3;
-  const int q = (y / HG_GROUPS) * 8 + (blockIdx.x & 7);
+  const int u = (y / HG_GROUPS) * 8 + (blockIdx.x & 7);
   const int hg = y % HG_GROUPS;
+  const int q = u / p.nsplit, sp = u % p.nsplit;
   if (q >= a.num_q) return;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave-uniform
@@ -118,7 +127,8 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_hg_kernel(MlaHgArgs p) {
   const int nvis = a.q_nvis[q];
   int cnt = a.count ? a.count[q] : a.k;
   cnt = max(0, min(cnt, min(a.k, nvis)));
-  const int nrows = cnt;
+  const int r0 = sp * p.rows_per_split;
+  const int nrows = max(0, min(cnt, r0 + p.rows_per_split) - r0);
   const int seq = a.q_seq[q];
   const uint32_t row0 = a.map.block_shift < 0 ? (uint32_t)a.map.seq_row0[seq] : 0u;
 
@@ -142,7 +152,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_hg_kernel(MlaHgArgs p) {
   constexpr int PER_THREAD = MLA_MAX_ROWS / MLA_THREADS;
   int bad = 0;
   if (nrows > 0) {  // block-uniform
-    const int32_t *ip = a.idx + (int64_t)q * a.k;
+    const int32_t *ip = a.idx + (int64_t)q * a.k + r0;
     int pos[PER_THREAD];
 #pragma unroll
     for (int j = 0; j < PER_THREAD; ++j) pos[j] = ip[min(tid + j * MLA_THREADS, nrows - 1)];
@@ -397,7 +407,11 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_hg_kernel(MlaHgArgs p) {
     for (int w = 0; w < MLA_WAVES; ++w)
       L += (mw[w][c] == -INFINITY) ? 0.0f : lw[w][c] * __builtin_amdgcn_exp2f(mw[w][c] - M);
     aex[wave][c] = (L > 0.0f) ? __builtin_amdgcn_exp2f(m_ref - M) / L : 0.0f;
-    if (wave == 0 && a.lse) a.lse[(int64_t)q * 128 + 32 * hg + c] = (L > 0.0f) ? M * LN2 + logf(L) : -INFINITY;
+    const float lse_v = (L > 0.0f) ? M * LN2 + logf(L) : -INFINITY;
+    if (wave == 0 && p.nsplit > 1)
+      p.part_lse[((int64_t)q * p.nsplit + sp) * 128 + 32 * hg + c] = lse_v;
+    else if (wave == 0 && a.lse)
+      a.lse[(int64_t)q * 128 + 32 * hg + c] = lse_v;
   }
   float fac[16];
   read_head_values(aex[wave], g, fac);  // this wavefront's own slot
@@ -410,7 +424,8 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_hg_kernel(MlaHgArgs p) {
     return reinterpret_cast<float *>(base + (w & 1) * HG_OREGION);
   };
   float *own = region(wave);
-  float *out = a.out + ((int64_t)q * 128 + 32 * hg) * 512;
+  float *out = (p.nsplit > 1 ? p.part_o + ((int64_t)q * p.nsplit + sp) * 128 * 512 : a.out + (int64_t)q * 128 * 512) +
+               (int64_t)32 * hg * 512;
 #pragma unroll
   for (int R = 0; R < 2; ++R) {
 #pragma unroll
@@ -440,12 +455,36 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_hg_kernel(MlaHgArgs p) {
   }
 }
 
-hipError_t launch_mla_hg(const MlaLaunch &a, float scale_log2, bool wide, hipStream_t st) {
+// Row splits S per head group for a decode batch (0: the head-group kernel is
+// not used).  48 to 64 queries fill 192 to 256 CUs with S = 1 and need no
+// partials.  Up to 32 queries take the largest S with 4 S workgroups per query
+// still at most 256 in all and at least 128 rows per split (one round on the
+// chip, a quarter of the row-split kernel's partial bytes at the same count).
+// 33 to 47 queries would leave a third of the CUs idle with S = 1 and take
+// two rounds with S = 2, so they stay on the row-split kernel.
+int mla_hg_splits(int num_q, int k, bool decode, bool dense) {
+  if (!decode || dense || num_q <= 0 || num_q > 64 || k < 128) return 0;
+  if (num_q >= 48) return 1;
+  if (num_q > 32) return 0;
+  return std::min(256 / (HG_GROUPS * num_q), k / 128);
+}
+
+int mla_hg_rows_per_split(int k, int nsplit) {
+  const int r = (k + nsplit - 1) / nsplit;
+  return (r + HG_T - 1) / HG_T * HG_T;
+}
+
+hipError_t launch_mla_hg(const MlaLaunch &a, float scale_log2, bool wide, int nsplit, float *part_o,
+                         float *part_lse, hipStream_t st) {
   MlaHgArgs p;
   p.a = a;
   p.scale_log2 = scale_log2;
-  const int64_t nq8 = (a.num_q + 7) / 8 * 8;  // a query's groups run on one XCD
-  const dim3 grid((unsigned)(nq8 * HG_GROUPS));
+  p.nsplit = nsplit;
+  p.rows_per_split = mla_hg_rows_per_split(a.k, nsplit);
+  p.part_o = part_o;
+  p.part_lse = part_lse;
+  const int64_t units8 = ((int64_t)a.num_q * nsplit + 7) / 8 * 8;  // (query, split) units, by XCD
+  const dim3 grid((unsigned)(units8 * HG_GROUPS));
   if (wide)
     hipLaunchKernelGGL(mla_hg_kernel<true>, grid, dim3(MLA_THREADS), 0, st, p);
   else

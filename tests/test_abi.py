@@ -63,7 +63,9 @@ def test_workspace_sizes():
     assert L.dsa_workspace_bytes(_lib.DSA_OP_TOPK, ctypes.byref(q_long), 2048) >= 64 * 262144 * 8  # candidate lists
     assert L.dsa_workspace_bytes(_lib.DSA_OP_MLA_PREFILL, ctypes.byref(q), 2048) == 0
     dec16 = L.dsa_workspace_bytes(_lib.DSA_OP_MLA_DECODE, ctypes.byref(q16), 2048)
-    assert dec16 >= 16 * 8 * 128 * 512 * 4  # eight row splits of fp32 partials
+    assert dec16 >= 16 * 4 * 128 * 512 * 4  # head groups, four row splits of fp32 partials
+    q40 = _queries(40, 131072)  # row splits over all heads
+    assert L.dsa_workspace_bytes(_lib.DSA_OP_MLA_DECODE, ctypes.byref(q40), 2048) >= 40 * 2 * 128 * 512 * 4
     # 64 queries split heads, not rows: no partials
     assert L.dsa_workspace_bytes(_lib.DSA_OP_MLA_DECODE, ctypes.byref(q), 2048) == 0
     assert L.dsa_workspace_bytes(_lib.DSA_OP_TOPK, ctypes.byref(q), 0) == ctypes.c_size_t(-1).value

@@ -1,11 +1,14 @@
 """GPU parity of the decode attention's head-group path against the oracle's
-sparse attention.  Decode batches of 48 to 64 queries split each query's 128
-heads over four workgroups of 32 that each attend over the whole selection
-and write final outputs (no row splits, no partials, no combine); these tests
-drive that path with partial and empty tiles, paged caches, positions outside
-the history, a NULL count array and a paged pool beyond 4 GiB, at the same
-tolerances as the other attention tests (max-abs <= 2e-2 * max|O|, mean-abs
-<= 5e-3 * mean|O| per query, lse within 2e-3)."""
+sparse attention.  Decode batches of up to 64 queries split each query's 128
+heads over four workgroups of 32.  From 48 to 64 queries each attends over the
+whole selection and writes final outputs (no partials, no combine); up to 32
+queries split the selection's rows as well (S splits, (O / l, lse) partials
+merged by the combine kernel); 33 to 47 and more than 64 queries take the
+row-split kernel.  These tests drive both forms with partial and empty tiles
+and splits, paged caches, positions outside the history, a NULL count array
+and a paged pool beyond 4 GiB, at the same tolerances as the other attention
+tests (max-abs <= 2e-2 * max|O|, mean-abs <= 5e-3 * mean|O| per query, lse
+within 2e-3)."""
 
 import numpy as np
 import pytest
@@ -20,7 +23,7 @@ pytestmark = pytest.mark.gpu
 
 
 def widen(seq_lens, n=48):
-    """The lengths repeated to n queries (the head-group path takes 48 to 64)."""
+    """The lengths repeated, or cut, to n queries."""
     reps = (n + len(seq_lens) - 1) // len(seq_lens)
     return (list(seq_lens) * reps)[:n]
 
@@ -88,39 +91,89 @@ def test_hg_positions_outside_history_are_skipped():
         check_out(out[i], o_ref, lse[i], l_ref, f"head groups out-of-range q{i}")
 
 
-def test_hg_same_queries_as_split_path():
-    """Eight queries alone take the row-split path (eight splits); the same
-    eight at the head of a 64-query batch take the head-group path.  Both attend over the same
+def _same_first_eight(n_other, n_hg, seed):
+    """Two batches whose first eight queries hold identical inputs and
+    selections, of n_other and n_hg queries; returns both runs' outputs."""
+    lens = [2100, 3000, 4096, 2500, 5000, 2048, 3333, 2222]
+    wa = make_custom(seq_lens=lens + [2600] * (n_other - 8), device="cuda", seed=seed)
+    wb = make_custom(seq_lens=lens + [2600] * (n_hg - 8), device="cuda", seed=seed)
+    wb.q_mla[:8] = wa.q_mla[:8]
+    for i, n in enumerate(lens):
+        ra, rb = int(wa.row0[i].item()), int(wb.row0[i].item())
+        wb.kv[rb:rb + n] = wa.kv[ra:ra + n]
+    ia, ca = random_selection(wa, 2048, seed + 1)
+    ib, cb = random_selection(wb, 2048, seed + 2)
+    ib[:8], cb[:8] = ia[:8], ca[:8]
+    a, la = run_mla(wa, ia, ca, 2048, True)
+    b, lb = run_mla(wb, ib, cb, 2048, True)
+    vmax = np.abs((bf16_bits(wa.kv).astype(np.uint32) << 16).view(np.float32)[:, :512]).max()
+    return a[:8], la[:8], b[:8], lb[:8], vmax
+
+
+@pytest.mark.parametrize("n_hg", [64, 8])
+def test_hg_same_queries_as_split_path(n_hg):
+    """Forty queries take the row-split path; the same first eight at the
+    head of a 64-query batch (head groups, one split) or alone (head groups,
+    eight row splits) take the head-group kernel.  All attend over the same
     rows, so only the rounding of P to bf16 (relative to different running
     maxima) may differ: at most 2^-9 of each weight."""
-    banner("mla head groups vs row splits")
-    lens = [2100, 3000, 4096, 2500, 5000, 2048, 3333, 2222]
-    wl8 = make_custom(seq_lens=lens, device="cuda", seed=65)
-    wl64 = make_custom(seq_lens=lens + [2600] * 56, device="cuda", seed=65)
-    # Same seed and leading lengths; copy the first eight queries' data over so
-    # that both batches hold identical inputs for them.
-    wl64.q_mla[:8] = wl8.q_mla
-    for i, n in enumerate(lens):
-        r8, r64 = int(wl8.row0[i].item()), int(wl64.row0[i].item())
-        wl64.kv[r64:r64 + n] = wl8.kv[r8:r8 + n]
-    idx8, cnt8 = random_selection(wl8, 2048, 16)
-    idx64, cnt64 = random_selection(wl64, 2048, 17)
-    idx64[:8], cnt64[:8] = idx8, cnt8
-    a, la = run_mla(wl8, idx8, cnt8, 2048, True)
-    b, lb = run_mla(wl64, idx64, cnt64, 2048, True)
-    vmax = np.abs((bf16_bits(wl8.kv).astype(np.uint32) << 16).view(np.float32)[:, :512]).max()
-    assert np.abs(a - b[:8]).max() <= 2.0 ** -8 * vmax
-    assert np.abs(la - lb[:8]).max() <= 1e-5 * np.abs(la).max()
+    banner(f"mla head groups ({n_hg} queries) vs row splits (40 queries)")
+    a, la, b, lb, vmax = _same_first_eight(40, n_hg, 65)
+    assert np.abs(a - b).max() <= 2.0 ** -8 * vmax
+    assert np.abs(la - lb).max() <= 1e-5 * np.abs(la).max()
 
 
-def test_hg_paged_pool_beyond_4gib():
-    """48 queries over a 4.4 GB paged pool whose block table alternates blocks
-    at its start and end (row offsets beyond 32 bits: the 64-bit gather form)."""
+@pytest.mark.parametrize("nq", [1, 5, 16, 20, 32])
+def test_hg_row_splits_small_batches(nq):
+    """Up to 32 queries: S = min(64 / nq, k / 128) row splits per head group
+    (16, 12, 4, 3 and 2 here; 12 takes the combine's general form)."""
+    banner(f"mla head groups with row splits: {nq} queries")
+    lens = [4096, 2049, 30000, 2500, 7000, 2048, 100000, 3001]
+    wl = make_custom(seq_lens=widen(lens, nq), device="cuda", seed=70 + nq, paged=nq % 2 == 0)
+    idx, cnt = random_selection(wl, 2048, 19 + nq)
+    compare(wl, idx, cnt, 2048, True, queries=sorted({0, nq // 2, nq - 1}))
+
+
+def test_hg_split_counts_around_split_edges():
+    """16 queries at k = 2048: four splits of 512 rows.  Counts on both sides
+    of each split boundary leave later splits empty or with one row; one row
+    in all is still returned exactly through the combine."""
+    banner("mla head groups: counts around split edges")
+    counts = [0, 1, 127, 128, 129, 511, 512, 513, 1024, 1025, 1535, 1536, 1537, 2000, 2047, 2048]
+    wl = make_custom(seq_lens=[3000] * 16, device="cuda", seed=66)
+    idx, cnt = random_selection(wl, 2048, 20, counts=np.array(counts, np.int32))
+    out, lse = run_mla(wl, idx, cnt, 2048, True)
+    ov = OracleView(wl)
+    for i, c in enumerate(counts):
+        if c == 0:
+            assert (out[i] == 0).all() and np.isneginf(lse[i]).all(), f"q{i}: empty selection"
+            continue
+        if c == 1:
+            row = int(wl.row0[i].item()) + int(idx[i, 0])
+            v = (bf16_bits(wl.kv[row]).astype(np.uint32) << 16).view(np.float32)[:512]
+            assert (out[i] == v[None, :]).all(), f"q{i}: one selected row must be returned exactly"
+        o_ref, l_ref = ov.mla(i, idx[i, :c])
+        check_out(out[i], o_ref, lse[i], l_ref, f"head-group splits q{i} count {c}")
+
+
+def test_hg_row_splits_count_null_k_1024():
+    banner("mla head groups with row splits: count NULL, k = 1024")
+    wl = make_custom(seq_lens=[700, 3000, 1024, 1500], device="cuda", seed=67)
+    idx, cnt = random_selection(wl, 1024, 21)
+    compare(wl, idx, cnt, 1024, True, with_count=False)
+
+
+@pytest.mark.parametrize("nq", [48, 40, 6])
+def test_hg_paged_pool_beyond_4gib(nq):
+    """A batch over a 4.4 GB paged pool whose block table alternates blocks
+    at its start and end (row offsets beyond 32 bits: the 64-bit gather form),
+    for each decode form: head groups (48), row splits (40), head groups with
+    row splits (6)."""
     from types import SimpleNamespace
-    banner("mla head groups: paged pool > 4 GiB")
+    banner(f"mla decode {nq} queries: paged pool > 4 GiB")
     bs, nblocks = 64, 59392                     # 3,801,088 rows x 1152 bytes = 4.38 GB
     rows = bs * nblocks
-    seq_len, nseq, nq = 4096, 2, 48
+    seq_len, nseq = 4096, 2
     per_seq = seq_len // bs
     low = np.arange(nseq * per_seq // 2)
     high = nblocks - 1 - np.arange(nseq * per_seq // 2)
@@ -139,6 +192,6 @@ def test_hg_paged_pool_beyond_4gib():
         q_nvis=torch.full((nq,), seq_len, dtype=torch.int32, device="cuda"), max_nvis=seq_len,
         block_size=bs, block_table=torch.from_numpy(table).cuda(), row0=None, softmax_scale=192 ** -0.5)
     idx, cnt = random_selection(wl, 2048, 18)
-    compare(wl, idx, cnt, 2048, True, queries=[0, 1, 47])
+    compare(wl, idx, cnt, 2048, True, queries=[0, 1, nq - 1])
     del kv
     torch.cuda.empty_cache()

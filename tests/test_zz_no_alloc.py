@@ -46,7 +46,7 @@ def _both(wl, k, seed):
 def test_noalloc_matches_workspace_call_twice_second_smaller():
     k = 2048
     ws_need = []
-    for nq, seed in ((80, 401), (16, 402)):  # 3 splits (60.1 MiB of partials), then 8 splits (32.1 MiB)
+    for nq, seed in ((80, 401), (16, 402)):  # 3 splits (60.1 MiB of partials), then 4 per head group (16.0 MiB)
         banner(f"noalloc decode: {nq} queries x 4096, k={k}")
         wl = make_custom(seq_lens=[4096] * nq, device="cuda", seed=seed)
         q = dsa.Queries(wl.q_seq, wl.q_nvis, wl.max_nvis)
