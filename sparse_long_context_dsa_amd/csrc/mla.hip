@@ -529,7 +529,8 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
 // Merge split partials: out = sum_s exp(lse_s - M) O_s / sum_s exp(lse_s - M).
 // NS > 0 fixes the split count at compile time, so that every partial's lse
 // and value are requested before the first is used (one memory round trip
-// instead of one per split); NS = 0 takes any count.  A split with no row
+// instead of one per split); NS < 0 does the same for any count up to -NS,
+// and NS = 0 takes any count, one split after the other.  A split with no row
 // (lse = -inf) has weight 0 and a zero partial; all splits empty gives 0 and
 // lse = -inf.
 template <int NS>
@@ -546,18 +547,24 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const float *__restric
   const float *po = part_o + ((int64_t)q * nsplit * 128 + head) * 512 + d;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float den = 0.0f, mx = -INFINITY;
-  if (NS > 0) {
-    float ls[NS > 0 ? NS : 1];
-    float4 v[NS > 0 ? NS : 1];
+  if (NS != 0) {
+    constexpr int M = NS > 0 ? NS : (NS < 0 ? -NS : 1);
+    float ls[M];
+    float4 v[M];
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      ls[s] = pl[s * 128];
-      v[s] = *reinterpret_cast<const float4 *>(po + (int64_t)s * 128 * 512);
+    for (int s = 0; s < M; ++s) {
+      if (NS > 0 || s < nsplit) {
+        ls[s] = pl[s * 128];
+        v[s] = *reinterpret_cast<const float4 *>(po + (int64_t)s * 128 * 512);
+      } else {
+        ls[s] = -INFINITY;
+        v[s] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
     }
 #pragma unroll
-    for (int s = 0; s < NS; ++s) mx = fmaxf(mx, ls[s]);
+    for (int s = 0; s < M; ++s) mx = fmaxf(mx, ls[s]);
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
+    for (int s = 0; s < M; ++s) {
       const float wgt = (ls[s] == -INFINITY) ? 0.0f : expf(ls[s] - mx);
       acc.x += wgt * v[s].x; acc.y += wgt * v[s].y; acc.z += wgt * v[s].z; acc.w += wgt * v[s].w;
       den += wgt;
@@ -677,8 +684,12 @@ hipError_t launch_mla(const MlaLaunch &a, bool decode, void *ws, hipStream_t st)
       hipLaunchKernelGGL(mla_combine_kernel<8>, cgrid, dim3(256), 0, st, p.part_o, p.part_lse, 8, a.num_q, a.out, a.lse);
       break;
     default:
-      hipLaunchKernelGGL(mla_combine_kernel<0>, cgrid, dim3(256), 0, st, p.part_o, p.part_lse, p.nsplit, a.num_q,
-                         a.out, a.lse);
+      if (p.nsplit <= 16)
+        hipLaunchKernelGGL(mla_combine_kernel<-16>, cgrid, dim3(256), 0, st, p.part_o, p.part_lse, p.nsplit,
+                           a.num_q, a.out, a.lse);
+      else
+        hipLaunchKernelGGL(mla_combine_kernel<0>, cgrid, dim3(256), 0, st, p.part_o, p.part_lse, p.nsplit, a.num_q,
+                           a.out, a.lse);
   }
   return hipGetLastError();
 }
