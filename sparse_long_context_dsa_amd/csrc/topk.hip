@@ -25,7 +25,8 @@
 // Kernels, chosen per batch by its longest history:
 //  * every row n <= 16384 (e.g. causal prefill): topk_row_kernel, one
 //    256-thread block per query; only the histograms live in LDS, so several
-//    rows are selected per CU at once.  The first-digit histogram comes from
+//    rows are selected per CU at once.  Batches of at most 256 rows take
+//    topk_row_wide_kernel instead, the same select with 1024 threads per row.  The first-digit histogram comes from
 //    the indexer's fused epilogue when available, else from LDS atomics.
 //  * some row longer (e.g. 128K decode): topk_long_kernel blocks of 16
 //    wavefronts, each owning 32768 consecutive positions (2048 per
@@ -48,6 +49,7 @@ namespace dsa {
 constexpr int LONG_THREADS = TOPK_LONG_WAVES * WAVE;
 constexpr int LONG_ROUNDS = TOPK_WAVE_SPAN / 512;  // rounds of 512 positions per wavefront
 constexpr int TAIL_CAP = 12288;                     // candidates the finishing block keeps in LDS
+constexpr int TOPK_ROW_WIDE_MAX_Q = 256;            // up to one row per CU: 1024-thread row blocks
 static_assert(TOPK_CHUNK == TOPK_ROW_MAX, "one histogram block covers one chunk");
 
 static inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -163,6 +165,16 @@ __global__ __launch_bounds__(TK_THREADS) __attribute__((amdgpu_waves_per_eu(3, 3
   row_select<TK_THREADS>(a, blockIdx.x, a.q_nvis[blockIdx.x], h, sm, sm64, res);
 }
 
+// The same selection with 1024 threads per row (16 keys per thread instead of
+// 64), for batches of at most as many rows as CUs, where each row has a CU to
+// itself anyway and the select's chain of passes sets the time.
+__global__ __launch_bounds__(LONG_THREADS) void topk_row_wide_kernel(SelectArgs a) {
+  __shared__ uint32_t h[TOPK_BINS];
+  __shared__ int sm[LONG_THREADS / WAVE];
+  __shared__ uint64_t sm64[LONG_THREADS / WAVE];
+  __shared__ int res[2];
+  row_select<LONG_THREADS>(a, blockIdx.x, a.q_nvis[blockIdx.x], h, sm, sm64, res);
+}
 
 // Lanes below this one in the wavefront (mbcnt over a ballot mask).
 __device__ __forceinline__ int lanes_below(uint64_t m) {
@@ -557,7 +569,10 @@ hipError_t launch_topk_select(const float *scores, int64_t ld, const int32_t *q_
   if (num_q == 0) return hipSuccess;
   SelectArgs a{scores, ld, q_nvis, k, hist1_valid ? 1 : 0, idx, count, ws};
   if (max_nvis <= TOPK_ROW_MAX) {  // every row fits one row block
-    hipLaunchKernelGGL(topk_row_kernel, dim3((unsigned)num_q), dim3(TK_THREADS), 0, st, a);
+    if (num_q <= TOPK_ROW_WIDE_MAX_Q)
+      hipLaunchKernelGGL(topk_row_wide_kernel, dim3((unsigned)num_q), dim3(LONG_THREADS), 0, st, a);
+    else
+      hipLaunchKernelGGL(topk_row_kernel, dim3((unsigned)num_q), dim3(TK_THREADS), 0, st, a);
     return hipGetLastError();
   }
   if (ws.nblk == 0) {  // rows up to TOPK_STREAM_MAX: one streaming block per row

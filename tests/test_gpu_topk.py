@@ -180,3 +180,30 @@ def test_many_rows_streaming_again():
         nvis.append(n)
         rows.append(v)
     assert_same(rows, nvis, 2048, "streaming, 130 rows")
+
+
+@pytest.mark.parametrize("nq", [5, 300])
+def test_short_rows_both_row_kernels(nq):
+    """Rows of at most 16384 positions: batches of up to 256 rows take the
+    1024-thread row kernel, larger ones the 256-thread one (several rows per
+    CU).  The same mix for both: integer ties, signed zeros, all equal, n
+    around k, the 16384 maximum."""
+    banner(f"topk short rows, {nq} rows")
+    rng = np.random.default_rng(47 + nq)
+    nvis, rows = [], []
+    for j in range(nq):
+        n = int(rng.choice([0, 1, 2047, 2048, 2049, 4096, 9000, 16384]))
+        kind = j % 4
+        if kind == 0:
+            v = rng.integers(0, 6, n).astype(np.float32)
+        elif kind == 1:
+            v = rng.choice(np.array([0.0, -0.0, 1.0, -1.0, 0.5], np.float32), n)
+        elif kind == 2:
+            v = np.full(n, 0.5, np.float32)
+        else:
+            v = rng.standard_normal(n).astype(np.float32)
+        nvis.append(n)
+        rows.append(v)
+    nvis[0], rows[0] = 16384, rng.standard_normal(16384).astype(np.float32)
+    assert_same(rows, nvis, 2048, f"short rows, {nq}")
+    assert_same(rows, nvis, 5, f"short rows, {nq}, k = 5")
