@@ -182,11 +182,13 @@ int dsa_topk(const dsa_queries *queries, const float *scores, int64_t ld, int32_
  *           z = softmax_scale * q . kv[r];
  *   lse   : fp32 [num_q, 128] natural-log sum of exp(z), or NULL.
  * An empty selection gives out = 0 and lse = -inf.
- * _decode gives a query several workgroups (for few queries): from 48 to 64
- * queries (k of a few hundred or more) four workgroups of 32 heads each that
- * attend over the whole selection and need no workspace, otherwise several
- * splits of the rows whose partial results are merged; _prefill gives each
- * query one workgroup (for many queries).  All compute the same function.
+ * _decode gives a query several workgroups (for few queries), with k >= 128:
+ * from 48 to 64 queries four workgroups of 32 heads each that attend over the
+ * whole selection and need no workspace; up to 32 queries four such head
+ * groups times several splits of the rows; otherwise several splits of the
+ * rows over all heads.  Row splits write partial results that a second pass
+ * merges.  _prefill gives each query one workgroup (for many queries).  All
+ * compute the same function.
  * ws : dsa_workspace_bytes(DSA_OP_MLA_DECODE or _PREFILL, queries, k) bytes
  * (0 is allowed for _prefill). */
 int dsa_sparse_mla_decode(const dsa_queries *queries, const dsa_kv_layout *layout,
@@ -204,10 +206,11 @@ int dsa_sparse_mla_decode(const dsa_queries *queries, const dsa_kv_layout *layou
  * Returns DSA_ERR_UNSUPPORTED, launching nothing, when this call's partials
  * (dsa_workspace_bytes(DSA_OP_MLA_DECODE, queries, k)) exceed the scratch:
  * for example 80 queries at k = 2048 fit (3 splits, 60.1 MiB), 285 queries
- * (2 splits, 142.8 MiB) do not, and 64 queries need none (head groups).  Every call on one GPU shares that GPU's
- * scratch, which keeps the last call's contents: calls that overlap in time
- * on one GPU (on different streams, or unordered across threads) race and
- * give wrong results; order them on one stream. */
+ * (2 splits, 142.8 MiB) do not, and 48 to 64 queries need none (head
+ * groups).  Every call on one GPU shares that GPU's scratch, which keeps
+ * the last call's contents: calls that overlap in time on one GPU (on
+ * different streams, or unordered across threads) race and give wrong
+ * results; order them on one stream. */
 #define DSA_NOALLOC_SCRATCH_BYTES ((size_t)72 << 20)
 int dsa_sparse_mla_decode_noalloc(const dsa_queries *queries, const dsa_kv_layout *layout,
                                   const uint16_t *q, const uint16_t *kv, const int32_t *idx,
