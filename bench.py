@@ -47,10 +47,10 @@ CALIB_BYTES = 1 << 30           # size of the calibration copy (read and written
 # same counter reads for the 1 GiB calibration copy.  Valid only for the kernel
 # source it was measured on: the figure is dropped when indexer.hip changes.
 INDEXER_TRAFFIC = {
-    "source_sha": "82f437e8cf8c2c95",
-    "fetch_kib": 542967, "write_kib": 35887,          # raw counter readings
+    "source_sha": "04097b2672ae4441",
+    "fetch_kib": 543038, "write_kib": 35887,          # raw counter readings
     "calib_fetch_kib": 524294, "calib_write_kib": 1048576,  # the 1 GiB copy
-    "bytes_per_launch": (542967 * 2 + 35887) * 1024,
+    "bytes_per_launch": (543038 * 2 + 35887) * 1024,
 }
 
 

@@ -15,7 +15,8 @@
 // indexer heads are the M side of v_mfma_scale_f32_16x16x128_f8f6f4 (4 M-tiles
 // of 16 heads, K = 128 = the whole head width, so one MFMA per 16x16 tile);
 // keys are the N side, 16 per tile, 4 tiles (64 keys) per step.  The query's
-// 8 KiB of FP8 q stays in registers for the whole run; keys stream from HBM
+// 8 KiB of FP8 q is read once per block into LDS and from there into each
+// wavefront's registers, where it stays for the whole run; keys stream from HBM
 // straight into the B-operand registers (each lane reads 32 contiguous bytes
 // of a key row; the two 64-byte halves of a row go to lane groups 0/1 and
 // 2/3), prefetched one step ahead into the other of two register buffers.
@@ -25,8 +26,8 @@
 // terms are summed in-lane; the remaining 4-way sum across lane groups is a
 // butterfly of vector-ALU lane swaps (v_permlane32_swap, v_permlane16_swap)
 // that also transposes, so lane l ends with the score of key s0+l.
-// Scores of four steps are staged in LDS and leave as 16-byte stores (1 KiB
-// per wavefront instruction).
+// Scores of four steps are staged in LDS and leave as non-temporal 16-byte
+// stores (1 KiB per wavefront instruction).
 //
 // Optionally each block also builds a 2048-bin histogram of the top 11 bits
 // of the scores' order-preserving keys (the first pass of the top-k radix
@@ -45,6 +46,8 @@ constexpr int IDX_WAVES = 4;
 constexpr int IDX_KPW_MIN = 256;                 // keys per wavefront: a multiple of 64,
 constexpr int IDX_KPW_MAX = 64 * WAVE;           // at most one 64-key step per lane
 constexpr int64_t IDX_MIN_WAVES = 32768;         // 32 wavefronts per SIMD
+
+typedef float nt_float4 __attribute__((ext_vector_type(4)));  // a vector type the nontemporal builtin takes
 
 struct KeyStep {
   v8i b[4];
@@ -116,28 +119,55 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SEL ? 2 : 3
   __shared__ __attribute__((aligned(16))) float sbuf[SEL ? 1 : IDX_WAVES][256];
   // SEL: the whole row's scores, by position.
   __shared__ __attribute__((aligned(16))) float rowbuf[SEL ? TOPK_ROW_MAX : 4];
+  // The query's 8 KiB of q, read once per block with contiguous 16-byte loads
+  // and shared by the four wavefronts through LDS (each wavefront reading it
+  // from memory in the operand layout took 4x the requests, 16 rows apart).
+  __shared__ __attribute__((aligned(16))) uint8_t qlds[SEL ? 16 : 64 * 128];
+  if (!SEL) {
+    static_assert(64 * 128 == 2 * 16 * IDX_WAVES * WAVE, "two 16-byte pieces per thread");
+    const uint4 *qsrc = reinterpret_cast<const uint4 *>(a.q8 + (int64_t)q * (64 * 128));
+    uint4 *qdst = reinterpret_cast<uint4 *>(qlds);
+    qdst[threadIdx.x] = qsrc[threadIdx.x];
+    qdst[threadIdx.x + IDX_WAVES * WAVE] = qsrc[threadIdx.x + IDX_WAVES * WAVE];
+  }
+  // The 64 epilogue weights w * q_scale, likewise once per block.
+  __shared__ __attribute__((aligned(16))) float wq[64];
+  if (threadIdx.x < 64) {
+    const float qs = a.q_scale ? a.q_scale[(int64_t)q * 64 + threadIdx.x] : 1.0f;
+    wq[threadIdx.x] = a.w[(int64_t)q * 64 + threadIdx.x] * qs;
+  }
   if (HIST || SEL) {
     for (int b = threadIdx.x; b < TOPK_BINS; b += blockDim.x) hist[b] = 0u;
-    __syncthreads();
   }
+  __syncthreads();
 
   // A operands: 4 M-tiles of 16 heads; lane holds head 16*mt + (lane&15),
   // bytes [32*(lane>>4), +32) of the 128-byte head row.
   const uint8_t *qp = a.q8 + (int64_t)q * (64 * 128);
   v8i A[4];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) A[mt] = load32(qp + (16 * mt + (lane & 15)) * 128 + 32 * (lane >> 4));
+  for (int mt = 0; mt < 4; ++mt) {
+    const int off = (16 * mt + (lane & 15)) * 128 + 32 * (lane >> 4);
+    if (SEL) {
+      A[mt] = load32(qp + off);
+    } else {
+      const uint4 x0 = *reinterpret_cast<const uint4 *>(qlds + off);
+      const uint4 x1 = *reinterpret_cast<const uint4 *>(qlds + off + 16);
+      A[mt][0] = (int)x0.x; A[mt][1] = (int)x0.y; A[mt][2] = (int)x0.z; A[mt][3] = (int)x0.w;
+      A[mt][4] = (int)x1.x; A[mt][5] = (int)x1.y; A[mt][6] = (int)x1.z; A[mt][7] = (int)x1.w;
+    }
+  }
   // Epilogue weights for the accumulator rows this lane holds:
   // head 16*mt + 4*(lane>>4) + r.
   float coef[4][4];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int h = 16 * mt + 4 * (lane >> 4) + r;
-      const float qs = a.q_scale ? a.q_scale[(int64_t)q * 64 + h] : 1.0f;
-      coef[mt][r] = a.w[(int64_t)q * 64 + h] * qs;
-    }
+  for (int mt = 0; mt < 4; ++mt) {
+    const float4 c4 = *reinterpret_cast<const float4 *>(&wq[16 * mt + 4 * (lane >> 4)]);
+    coef[mt][0] = c4.x;
+    coef[mt][1] = c4.y;
+    coef[mt][2] = c4.z;
+    coef[mt][3] = c4.w;
+  }
 
   const int s_begin = (chunk * IDX_WAVES + wave) * kpw;
   const int s_end = min(s_begin + kpw, nvis);
@@ -156,7 +186,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SEL ? 2 : 3
     const float4 v = *reinterpret_cast<const float4 *>(&sbuf[wave][4 * lane]);
     const int p0 = g0 + 4 * lane;
     if (p0 + 3 < s_end) {
-      *reinterpret_cast<float4 *>(srow + p0) = v;
+      // Non-temporal: the scores are read back once, by the top-k, and should
+      // not displace the key stream's lines on the way.
+      const nt_float4 v4 = {v.x, v.y, v.z, v.w};
+      __builtin_nontemporal_store(v4, reinterpret_cast<nt_float4 *>(srow + p0));
     } else {
       const float vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
