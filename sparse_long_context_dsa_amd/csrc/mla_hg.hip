@@ -282,18 +282,23 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_hg_kernel(MlaHgArgs p) {
     mfma16_drain(s0, s1);
   };
 
-  auto pv = [&](const uint8_t *buf, const uint4 &pa) {
-    constexpr int AH = 4;
-    auto v_frag = [&](const int nt) {
-      const int o0 = tr_base[nt & 1][0] + 1024 * (nt >> 1), o1 = tr_base[nt & 1][1] + 1024 * (nt >> 1);
-      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)(buf + o0));
-      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)(buf + o1));
-      const uint2 ulo = __builtin_bit_cast(uint2, lo), uhi = __builtin_bit_cast(uint2, hi);
-      return make_uint4(ulo.x, ulo.y, uhi.x, uhi.y);
-    };
+  // PV's V fragments (dims 32 nt .. +31 of the tile's 16 rows) by the
+  // transposing read.  The first PV_AH are read before the softmax, which
+  // hides their latency.
+  constexpr int PV_AH = 4;
+  auto v_frag_at = [&](const uint8_t *buf, const int nt) {
+    const int o0 = tr_base[nt & 1][0] + 1024 * (nt >> 1), o1 = tr_base[nt & 1][1] + 1024 * (nt >> 1);
+    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)(buf + o0));
+    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s *)(buf + o1));
+    const uint2 ulo = __builtin_bit_cast(uint2, lo), uhi = __builtin_bit_cast(uint2, hi);
+    return make_uint4(ulo.x, ulo.y, uhi.x, uhi.y);
+  };
+  auto pv = [&](const uint8_t *buf, const uint4 &pa, const uint4 (&v0)[PV_AH]) {
+    constexpr int AH = PV_AH;
+    auto v_frag = [&](const int nt) { return v_frag_at(buf, nt); };
     uint4 vf[AH + 1];
 #pragma unroll
-    for (int nt = 0; nt < AH; ++nt) vf[nt] = v_frag(nt);
+    for (int nt = 0; nt < AH; ++nt) vf[nt] = v0[nt];
 #pragma unroll
     for (int nt = 0; nt < 16; ++nt) {
       if (nt + AH < 16) vf[(nt + AH) % (AH + 1)] = v_frag(nt + AH);
@@ -331,6 +336,9 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_hg_kernel(MlaHgArgs p) {
 
     v4f s0, s1;
     qk(buf, s0, s1);
+    uint4 v0[PV_AH];
+#pragma unroll
+    for (int nt = 0; nt < PV_AH; ++nt) v0[nt] = v_frag_at(buf, nt);
     // Lane rows: after the swap lane l holds head 32 hg + l % 32, tile rows
     // 8 (l / 32) + e in z[e] (e = 0..7).
     float z[8];
@@ -380,7 +388,7 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_hg_kernel(MlaHgArgs p) {
       if (g == 0) aex[wave][c] = alpha;  // own slot: no other wavefront reads it
       rescale_o(aex[wave]);
     }
-    pv(buf, pa);
+    pv(buf, pa, v0);
   };
 
   if (ntw > 0) issue_tile(wave, tb0[wave]);
