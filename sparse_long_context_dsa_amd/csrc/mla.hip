@@ -584,7 +584,13 @@ __global__ __launch_bounds__(256) void mla_combine_kernel(const float *__restric
   }
   const float inv = den > 0.0f ? 1.0f / den : 0.0f;
   float4 r = make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-  *reinterpret_cast<float4 *>(out + ((int64_t)q * 128 + head) * 512 + d) = r;
+  {
+    // Non-temporal: the output is not read again in the step, and its dirty
+    // lines would otherwise be written back while the next indexer streams.
+    typedef float ntf4 __attribute__((ext_vector_type(4)));
+    const ntf4 v4 = {r.x, r.y, r.z, r.w};
+    __builtin_nontemporal_store(v4, reinterpret_cast<ntf4 *>(out + ((int64_t)q * 128 + head) * 512 + d));
+  }
   if (lse && (threadIdx.x & 127) == 0) lse[(int64_t)q * 128 + head] = den > 0.0f ? mx + logf(den) : -INFINITY;
 }
 
