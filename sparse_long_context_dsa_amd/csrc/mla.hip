@@ -520,7 +520,15 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_kernel(MlaKernelArgs p) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int h = 32 * wave + 8 * i + 4 * g + j;
-          obase[(int64_t)h * 512 + 32 * nt + c] = read_scaled(o[nt][4 * i + j], il[4 * i + j]);
+          {
+            // Split partials (read once, by the combine) non-temporally; the
+            // prefill output measured slower that way.
+            const float v = read_scaled(o[nt][4 * i + j], il[4 * i + j]);
+            if (p.nsplit > 1)
+              __builtin_nontemporal_store(v, obase + (int64_t)h * 512 + 32 * nt + c);
+            else
+              obase[(int64_t)h * 512 + 32 * nt + c] = v;
+          }
         }
   }
   if (lbase && g == 0) lbase[head] = lse_v;

@@ -457,14 +457,11 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_hg_kernel(MlaHgArgs p) {
         acc.z += v.z;
         acc.w += v.w;
       }
-      float *dst = out + (int64_t)h * 512 + 256 * R + 4 * lane;
-      if (p.nsplit == 1) {  // final output, not read again in the step: non-temporal (see the combine)
-        typedef float ntf4 __attribute__((ext_vector_type(4)));
-        const ntf4 v4 = {acc.x, acc.y, acc.z, acc.w};
-        __builtin_nontemporal_store(v4, reinterpret_cast<ntf4 *>(dst));
-      } else {
-        *reinterpret_cast<float4 *>(dst) = acc;
-      }
+      // Non-temporal, both the final output (not read again in the step) and
+      // the split partials (read once, by the combine).
+      typedef float ntf4 __attribute__((ext_vector_type(4)));
+      const ntf4 v4 = {acc.x, acc.y, acc.z, acc.w};
+      __builtin_nontemporal_store(v4, reinterpret_cast<ntf4 *>(out + (int64_t)h * 512 + 256 * R + 4 * lane));
     }
     if (R == 0) __syncthreads();
   }
