@@ -134,15 +134,21 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_hg_kernel(MlaHgArgs p) {
 
   // q of the group's 32 heads, as B fragments of S^T = K . Q^T: lane l holds
   // head 32 hg + 16 hb + l % 16, dims 32 ks + 8 (l / 16) .. + 7.  Every
-  // wavefront needs all of them.  Requested after the position loads and
-  // before their values are used, so that the latencies overlap.
+  // wavefront needs all of them.  The group's 36 KiB are read once, by
+  // direct-to-LDS loads of whole lines (requested after the position loads,
+  // so that the latencies overlap), into the second tile buffers (free until
+  // the first step), and read from there by each wavefront.
+  constexpr int Q_PARTS = 32 * ROW_BYTES / 1024 / MLA_WAVES;  // 9 KiB-loads per wavefront
+  static_assert(Q_PARTS * 1024 * MLA_WAVES == 32 * ROW_BYTES && 32 * ROW_BYTES <= sizeof(tb1), "q stage fits");
   uint4 qb[2][18];
   auto load_q = [&]() {
-    const uint16_t *qr = a.q + ((int64_t)q * 128 + 32 * hg + (lane & 15)) * 576 + 8 * (lane >> 4);
+    const uint8_t *qg = reinterpret_cast<const uint8_t *>(a.q + ((int64_t)q * 128 + 32 * hg) * 576);
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-      for (int ks = 0; ks < 18; ++ks) qb[hb][ks] = *reinterpret_cast<const uint4 *>(qr + hb * 16 * 576 + 32 * ks);
+    for (int j = 0; j < Q_PARTS; ++j) {
+      const int part = wave * Q_PARTS + j;
+      __builtin_amdgcn_global_load_lds(qg + 1024 * part + 16 * lane, (lds_void *)(&tb1[0][0] + 1024 * part), 16, 0,
+                                       0);
+    }
   };
 
   // Selected positions -> physical rows (all of a thread's positions, then
@@ -198,6 +204,12 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_hg_kernel(MlaHgArgs p) {
   }
   const bool any_bad = (bad_w[0] | bad_w[1] | bad_w[2] | bad_w[3]) != 0;
   static_assert(MLA_WAVES == 4, "any_bad reads four wavefront words");
+  auto bare_barrier = []() {  // LDS operations done, loads (and gathers) left in flight
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  };
 
   // This wavefront's tiles: j = wave + 4 i, i < ntw.
   const int nt16 = (nrows + HG_T - 1) / HG_T;
@@ -392,6 +404,19 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_hg_kernel(MlaHgArgs p) {
   };
 
   if (ntw > 0) issue_tile(wave, tb0[wave]);
+  // q through the stage: the gather of the first tile is already on its way
+  // (its loads are younger than those of q, so waiting for q leaves it).
+  {
+    if (ntw > 0) hg_wait_vm<HG_PARTS>(); else hg_wait_vm<0>();
+    bare_barrier();
+    const uint8_t *sb = &tb1[0][0] + (lane & 15) * ROW_BYTES + 16 * (lane >> 4);
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int ks = 0; ks < 18; ++ks)
+        qb[hb][ks] = *reinterpret_cast<const uint4 *>(sb + hb * 16 * ROW_BYTES + 64 * ks);
+    bare_barrier();  // every wavefront has its q before any gather refills the stage
+  }
   for (int i = 0; i < ntw; i += 2) {
     step(i, tb0[wave], tb1[wave]);
     if (i + 1 < ntw) step(i + 1, tb1[wave], tb0[wave]);
