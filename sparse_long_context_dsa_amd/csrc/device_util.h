@@ -65,15 +65,37 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ int wave_inclusive_scan(int v) {
-  const int lane = threadIdx.x & (WAVE - 1);
-#pragma unroll
-  for (int d = 1; d < WAVE; d <<= 1) {
-    const int o = __shfl_up(v, d, WAVE);
-    if (lane >= d) v += o;
-  }
+// Inclusive prefix sums over the 64 lanes of a wavefront from DPP moves
+// (six dependent ALU steps, no trip through the LDS crossbar as a lane
+// shuffle takes): row_shr 1, 2, 4, 8 make the sums within each row of 16
+// lanes, then row_bcast:15 adds row 0's total to row 1 and row 2's to row 3,
+// and row_bcast:31 adds the total of rows 0 and 1 to rows 2 and 3.  A lane
+// with no source lane, or in a row the row mask leaves out, receives 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_or_zero(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t dpp_or_zero(uint64_t v) {
+  const uint32_t lo = dpp_or_zero<CTRL, ROW_MASK>((uint32_t)v);
+  const uint32_t hi = dpp_or_zero<CTRL, ROW_MASK>((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+constexpr int DPP_ROW_SHR = 0x110, DPP_ROW_BCAST15 = 0x142, DPP_ROW_BCAST31 = 0x143;
+template <typename U>
+__device__ __forceinline__ U wave_inclusive_scan_u(U v) {
+  v += dpp_or_zero<DPP_ROW_SHR + 1, 0xF>(v);
+  v += dpp_or_zero<DPP_ROW_SHR + 2, 0xF>(v);
+  v += dpp_or_zero<DPP_ROW_SHR + 4, 0xF>(v);
+  v += dpp_or_zero<DPP_ROW_SHR + 8, 0xF>(v);
+  v += dpp_or_zero<DPP_ROW_BCAST15, 0xA>(v);
+  v += dpp_or_zero<DPP_ROW_BCAST31, 0xC>(v);
   return v;
 }
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  return (int)wave_inclusive_scan_u<uint32_t>((uint32_t)v);
+}
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) { return wave_inclusive_scan_u<uint32_t>(v); }
+__device__ __forceinline__ uint64_t wave_inclusive_scan(uint64_t v) { return wave_inclusive_scan_u<uint64_t>(v); }
 
 }  // namespace dsa

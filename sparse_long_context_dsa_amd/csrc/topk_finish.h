@@ -29,8 +29,9 @@ struct FinishLds {
 };
 
 // Finishes row q (n > TOPK_ROW_MAX positions, k <= n) with one block of NT
-// threads.  after_issue() runs right after the candidates' loads are issued
-// and before any of them is used, so that a caller's own loads overlap them.
+// threads.  after_issue() runs once the first loads (counts, histograms and
+// the first list entries) are in flight, so that a caller's own loads
+// overlap them.
 // emit(o, position) receives the o-th chosen position, o ascending; returns
 // the count (k).  Every thread of the block calls it (it has block barriers).
 template <int NT, typename AfterIssue, typename Emit>
@@ -40,6 +41,8 @@ __device__ int finish_row(const TopkWs &ws, const int q, const int n, const int 
   constexpr int BPT = TOPK_BINS / NT;                   // histogram bins per thread
   constexpr int NW = NT / WAVE;
   constexpr int LB = 16;                                // lists per wavefront per load batch
+  constexpr int LB0 = 4;   // lists per wavefront requested with the counts (NW * LB0 cover 2^17 positions at NW = 16)
+  constexpr int E0 = 2;    // their entries per lane requested then: a 2048-position list rarely holds more than 128
   const int t = threadIdx.x;
   const int lane = t & (WAVE - 1), wave = t / WAVE;
   const int nblk = ws.nblk;
@@ -49,16 +52,30 @@ __device__ int finish_row(const TopkWs &ws, const int q, const int n, const int 
   const uint32_t *gw = ws.wcnt + (int64_t)q * nblk * TOPK_LONG_WAVES;
   const uint2 *cq = ws.cand + (int64_t)q * nblk * TOPK_LONG_SPAN;
   const uint32_t *h2 = ws.hist2 + (int64_t)q * nblk * TOPK_BINS;
-  // Everything that depends on nothing else is requested at once: the list
-  // counts and every span's digit-2 histogram (summed: the row's histogram
-  // of the second digit over the keys of bin B1).
+  // Everything that depends on nothing else is requested at once, with no
+  // branch around a load (a conditional load makes the compiler wait for all
+  // earlier loads where its value merges): the list counts, the first
+  // entries of this wavefront's first LB0 lists (wavefront w takes lists w,
+  // w + NW, ...; lane j entries j and j + WAVE), before the counts say how many
+  // of them are real, and every span's digit-2 histogram (summed: the row's
+  // histogram of the second digit over the keys of bin B1).  Indices past the
+  // row's lists or spans are clamped to its last one, so every load stays
+  // inside the row's part of the workspace, and their values are dropped.
   int c[SEG];
   int local = 0;
 #pragma unroll
   for (int j = 0; j < SEG; ++j) {
     const int sg = t * SEG + j;
-    c[j] = sg < nseg ? (int)gw[sg] : 0;
+    const int v = (int)gw[min(sg, nseg - 1)];
+    c[j] = sg < nseg ? v : 0;
     local += c[j];
+  }
+  uint2 e0[LB0][E0];
+#pragma unroll
+  for (int b = 0; b < LB0; ++b) {
+    const int l = min(wave + b * NW, nseg - 1);
+#pragma unroll
+    for (int e = 0; e < E0; ++e) e0[b][e] = cq[(int64_t)l * TOPK_WAVE_SPAN + lane + WAVE * e];
   }
   uint32_t hb[BPT];
 #pragma unroll
@@ -68,11 +85,11 @@ __device__ int finish_row(const TopkWs &ws, const int q, const int n, const int 
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int i = 0; i < BPT; ++i) u[j][i] = c0 + j < nb ? h2[(int64_t)(c0 + j) * TOPK_BINS + t + i * NT] : 0u;
+      for (int i = 0; i < BPT; ++i) u[j][i] = h2[(int64_t)min(c0 + j, nb - 1) * TOPK_BINS + t + i * NT];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int i = 0; i < BPT; ++i) hb[i] += u[j][i];
+      for (int i = 0; i < BPT; ++i) hb[i] += c0 + j < nb ? u[j][i] : 0u;
   }
   int ntot;
   int ex = block_exclusive_scan<NT>(local, s.sm, ntot);
@@ -102,17 +119,31 @@ __device__ int finish_row(const TopkWs &ws, const int q, const int n, const int 
     }
     return cq[(int64_t)lo * TOPK_WAVE_SPAN + (i - s.off[lo])];
   };
-  // Into LDS: wavefront w copies lists w, w + NW, ..., LB lists per batch,
-  // lane j taking entry j of each (a list rarely holds more than a
-  // wavefront's worth; the rest follow entry by entry).  The caller's loads go
-  // out right after the first batch's.
-  auto batch = [&](int l0, uint2 *e, int *dst) {
+  // Into LDS.  The first LB0 lists of each wavefront come from registers
+  // (e0); entries past E0 * WAVE, and the lists of longer rows (LB per
+  // wavefront per batch, lane j taking entry j of each), follow from memory.
+  auto slots = [&](int l0, int *dst) {
 #pragma unroll
     for (int b = 0; b < LB; ++b) {
       const int l = l0 + b * NW;
       const int beg = l < nseg ? s.off[l] : 0, cnt = l < nseg ? s.off[l + 1] - beg : 0;
       dst[b] = lane < cnt ? beg + lane : -1;
-      e[b] = lane < cnt ? cq[(int64_t)l * TOPK_WAVE_SPAN + lane] : make_uint2(0u, 0u);
+    }
+  };
+  auto batch = [&](int l0, uint2 *e, int *dst) {
+    slots(l0, dst);
+#pragma unroll
+    for (int b = 0; b < LB; ++b) {
+      const int l = l0 + b * NW;
+      e[b] = dst[b] >= 0 ? cq[(int64_t)l * TOPK_WAVE_SPAN + lane] : make_uint2(0u, 0u);
+    }
+  };
+  // Entries from `from` on of list l, one per lane and round.
+  auto rest = [&](int l, int beg, int cnt, int from) {
+    for (int j = lane + from; j < cnt; j += WAVE) {
+      const uint2 x = cq[(int64_t)l * TOPK_WAVE_SPAN + j];
+      s.ck[beg + j] = x.x;
+      s.cpos[beg + j] = x.y;
     }
   };
   auto put = [&](int l0, const uint2 *e, const int *dst) {
@@ -123,26 +154,37 @@ __device__ int finish_row(const TopkWs &ws, const int q, const int n, const int 
         s.cpos[dst[b]] = e[b].y;
       }
       const int l = l0 + b * NW;
-      const int beg = l < nseg ? s.off[l] : 0, cnt = l < nseg ? s.off[l + 1] - beg : 0;
-      for (int j = lane + WAVE; j < cnt; j += WAVE) {
-        const uint2 x = cq[(int64_t)l * TOPK_WAVE_SPAN + j];
-        s.ck[beg + j] = x.x;
-        s.cpos[beg + j] = x.y;
-      }
+      if (l < nseg) rest(l, s.off[l], s.off[l + 1] - s.off[l], WAVE);
     }
   };
+  after_issue();
   if (in_lds) {
-    uint2 e[LB];
+#pragma unroll
+    for (int b = 0; b < LB0; ++b) {
+      const int l = wave + b * NW;
+      if (l < nseg) {  // wave-uniform
+        const int beg = s.off[l], cnt = s.off[l + 1] - beg;
+#pragma unroll
+        for (int e = 0; e < E0; ++e) {
+          const int j = lane + WAVE * e;
+          if (j < cnt) {
+            s.ck[beg + j] = e0[b][e].x;
+            s.cpos[beg + j] = e0[b][e].y;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < LB0; ++b) {
+      const int l = wave + b * NW;
+      if (l < nseg) rest(l, s.off[l], s.off[l + 1] - s.off[l], E0 * WAVE);
+    }
     int dst[LB];
-    batch(wave, e, dst);
-    after_issue();
-    put(wave, e, dst);
-    for (int l0 = wave + NW * LB; l0 < nseg; l0 += NW * LB) {
+    uint2 e[LB];
+    for (int l0 = wave + NW * LB0; l0 < nseg; l0 += NW * LB) {
       batch(l0, e, dst);
       put(l0, e, dst);
     }
-  } else {
-    after_issue();
   }
   lds_barrier();
   auto key_of = [&](int i) { return in_lds ? s.ck[i] : locate(i).x; };

@@ -33,12 +33,7 @@ template <int NT, typename T>
 __device__ __forceinline__ T block_exclusive_scan(T v, T *sm, T &total) {
   constexpr int W = NT / WAVE;
   const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x / WAVE;
-  T inc = v;
-#pragma unroll
-  for (int d = 1; d < WAVE; d <<= 1) {
-    const T o = __shfl_up(inc, d, WAVE);
-    if (lane >= d) inc += o;
-  }
+  const T inc = wave_inclusive_scan(v);
   if (lane == WAVE - 1) sm[wave] = inc;
   lds_barrier();
   T before = 0, tot = 0;
