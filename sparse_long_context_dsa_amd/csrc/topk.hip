@@ -248,6 +248,8 @@ __global__ __launch_bounds__(ST_THREADS) void topk_stream_kernel(SelectArgs a) {
   __shared__ uint32_t bm[ST_WORDS];  // selected positions
   __shared__ uint32_t tbm[ST_WORDS]; // positions whose key equals the k-th
   __shared__ int ncand;
+  __shared__ int bidx[WAVE];         // boundary candidates ranked directly
+  __shared__ int nbnd;
   int32_t *out = a.idx + (int64_t)q * k;
   const float *row = a.scores + (int64_t)q * a.ld;
   uint32_t *gh = a.ws.hist + (int64_t)q * TOPK_BINS;
@@ -281,18 +283,15 @@ __global__ __launch_bounds__(ST_THREADS) void topk_stream_kernel(SelectArgs a) {
   };
 #pragma unroll
   for (int u = 0; u < ST_D; ++u) load_round(u, f[u]);
-  int hsum = 0;
 #pragma unroll
-  for (int i = 0; i < TOPK_BINS / ST_THREADS; ++i) {
-    h[t + i * ST_THREADS] = hv[i];
-    hsum += (int)hv[i];
-  }
+  for (int i = 0; i < TOPK_BINS / ST_THREADS; ++i) h[t + i * ST_THREADS] = hv[i];
   if (t == 0) ncand = 0;
-  int htot;
-  block_exclusive_scan<ST_THREADS>(hsum, sm, htot);
-  if (htot != n) rebuild_first_digit<ST_THREADS>(row, n, h);  // block-uniform: not only this call's counts
   __syncthreads();
-  find_rank_bin<ST_THREADS, TOPK_BINS>(h, k, sm, res);
+  if (find_rank_bin<ST_THREADS, TOPK_BINS>(h, k, sm, res) != n) {  // block-uniform: not only this call's counts
+    rebuild_first_digit<ST_THREADS>(row, n, h);
+    __syncthreads();
+    find_rank_bin<ST_THREADS, TOPK_BINS>(h, k, sm, res);
+  }
   const uint32_t b1 = (uint32_t)res[0];
   const int r = k - res[1];
 
@@ -361,51 +360,78 @@ __global__ __launch_bounds__(ST_THREADS) void topk_stream_kernel(SelectArgs a) {
   find_rank_bin<ST_THREADS, TOPK_BINS>(h, r, sm, res);
   const uint32_t pre = (b1 << 11) | (uint32_t)res[0];
   const int r2 = r - res[1];
-  __syncthreads();
-  // Digit 3: key[9:0] of the candidates with key[31:10] == pre.
-  zero_lds<ST_THREADS>(h, 1024);
-  __syncthreads();
-  for_each([&](uint32_t kk, uint32_t) {
-    if ((kk >> 10) == pre) atomicAdd(&h[kk & 1023u], 1u);
-  });
-  __syncthreads();
-  find_rank_bin<ST_THREADS, 1024>(h, r2, sm, res);
-  const uint32_t kth = (pre << 10) | (uint32_t)res[0];
-  const int ties = r2 - res[1];
-  const int tie_total = (int)h[res[0]];
-  // Mark keys above the k-th, and keys equal to it, in position bitmaps.
-#pragma unroll
-  for (int i = 0; i < ST_WORDS_PER_THREAD; ++i) {
-    bm[t * ST_WORDS_PER_THREAD + i] = 0u;
-    tbm[t * ST_WORDS_PER_THREAD + i] = 0u;
-  }
-  __syncthreads();
-  for_each([&](uint32_t kk, uint32_t p) {
-    if (kk > kth) atomicOr(&bm[p >> 5], 1u << (p & 31));
-    else if (kk == kth) atomicOr(&tbm[p >> 5], 1u << (p & 31));
-  });
-  __syncthreads();
+  const int nbound = (int)h[res[0]];  // candidates with key[31:10] == pre
   // Thread t owns bitmap words [4t, 4t + 4), positions [128t, 128t + 128):
-  // thread order is position order.
+  // thread order is position order.  w: the chosen keys equal to the k-th.
   uint32_t w[ST_WORDS_PER_THREAD];
-#pragma unroll
-  for (int i = 0; i < ST_WORDS_PER_THREAD; ++i) w[i] = tbm[t * ST_WORDS_PER_THREAD + i];
-  if (ties < tie_total) {  // block-uniform: only the `ties` lowest positions among the ties
-    int c = 0;
-#pragma unroll
-    for (int i = 0; i < ST_WORDS_PER_THREAD; ++i) c += __popc(w[i]);
-    int tt;
-    int rank = block_exclusive_scan<ST_THREADS>(c, sm, tt);
+  if (!over && nbound <= WAVE) {  // block-uniform
+    // Few candidates share the boundary prefix (the usual case): one
+    // wavefront ranks them by (key descending, position ascending) and marks
+    // the chosen r2, so neither the third digit nor a tie bitmap is needed.
 #pragma unroll
     for (int i = 0; i < ST_WORDS_PER_THREAD; ++i) {
-      uint32_t m = w[i], keep = 0u;
-      while (m) {
-        const uint32_t bit = m & (0u - m);
-        if (rank < ties) keep |= bit;
-        ++rank;
-        m ^= bit;
+      bm[t * ST_WORDS_PER_THREAD + i] = 0u;
+      w[i] = 0u;
+    }
+    if (t == 0) nbnd = 0;
+    __syncthreads();
+    for (int i = t; i < ntot; i += ST_THREADS) {
+      const uint32_t kk = ck[i] >> 10, p = cpos[i];
+      if (kk > pre) atomicOr(&bm[p >> 5], 1u << (p & 31));
+      else if (kk == pre) bidx[atomicAdd(&nbnd, 1)] = i;
+    }
+    __syncthreads();
+    if (t < WAVE) {
+      const bool have = t < nbound;
+      const uint32_t mk = have ? ck[bidx[t]] : 0u, mp = have ? cpos[bidx[t]] : 0u;
+      const int rank = boundary_rank(mk, mp, nbound);
+      if (have && rank < r2) atomicOr(&bm[mp >> 5], 1u << (mp & 31));
+    }
+    __syncthreads();
+  } else {
+    __syncthreads();
+    // Digit 3: key[9:0] of the candidates with key[31:10] == pre.
+    zero_lds<ST_THREADS>(h, 1024);
+    __syncthreads();
+    for_each([&](uint32_t kk, uint32_t) {
+      if ((kk >> 10) == pre) atomicAdd(&h[kk & 1023u], 1u);
+    });
+    __syncthreads();
+    find_rank_bin<ST_THREADS, 1024>(h, r2, sm, res);
+    const uint32_t kth = (pre << 10) | (uint32_t)res[0];
+    const int ties = r2 - res[1];
+    const int tie_total = (int)h[res[0]];
+    // Mark keys above the k-th, and keys equal to it, in position bitmaps.
+#pragma unroll
+    for (int i = 0; i < ST_WORDS_PER_THREAD; ++i) {
+      bm[t * ST_WORDS_PER_THREAD + i] = 0u;
+      tbm[t * ST_WORDS_PER_THREAD + i] = 0u;
+    }
+    __syncthreads();
+    for_each([&](uint32_t kk, uint32_t p) {
+      if (kk > kth) atomicOr(&bm[p >> 5], 1u << (p & 31));
+      else if (kk == kth) atomicOr(&tbm[p >> 5], 1u << (p & 31));
+    });
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < ST_WORDS_PER_THREAD; ++i) w[i] = tbm[t * ST_WORDS_PER_THREAD + i];
+    if (ties < tie_total) {  // block-uniform: only the `ties` lowest positions among the ties
+      int c = 0;
+#pragma unroll
+      for (int i = 0; i < ST_WORDS_PER_THREAD; ++i) c += __popc(w[i]);
+      int tt;
+      int rank = block_exclusive_scan<ST_THREADS>(c, sm, tt);
+#pragma unroll
+      for (int i = 0; i < ST_WORDS_PER_THREAD; ++i) {
+        uint32_t m = w[i], keep = 0u;
+        while (m) {
+          const uint32_t bit = m & (0u - m);
+          if (rank < ties) keep |= bit;
+          ++rank;
+          m ^= bit;
+        }
+        w[i] = keep;
       }
-      w[i] = keep;
     }
   }
   int c = 0;
@@ -475,17 +501,14 @@ __global__ __launch_bounds__(LONG_THREADS) void topk_long_kernel(SelectArgs a) {
   // every block of the row alike; the first block publishes it for the finish.
   // A histogram that does not sum to n (the workspace held other data) is
   // rebuilt by every block of the row from the whole row, alike.
-  int hsum = 0;
 #pragma unroll
-  for (int i = 0; i < TOPK_BINS / LONG_THREADS; ++i) {
-    h[t + i * LONG_THREADS] = hv[i];
-    hsum += (int)hv[i];
-  }
-  int htot;
-  block_exclusive_scan<LONG_THREADS>(hsum, sm, htot);
-  if (htot != n) rebuild_first_digit<LONG_THREADS>(row, n, h);  // block-uniform
+  for (int i = 0; i < TOPK_BINS / LONG_THREADS; ++i) h[t + i * LONG_THREADS] = hv[i];
   __syncthreads();
-  find_rank_bin<LONG_THREADS, TOPK_BINS>(h, k, sm, res);
+  if (find_rank_bin<LONG_THREADS, TOPK_BINS>(h, k, sm, res) != n) {  // block-uniform
+    rebuild_first_digit<LONG_THREADS>(row, n, h);
+    __syncthreads();
+    find_rank_bin<LONG_THREADS, TOPK_BINS>(h, k, sm, res);
+  }
   const uint32_t b1 = (uint32_t)res[0];
   if (c == 0 && t == 0) a.ws.b1info[q] = make_uint2((uint32_t)res[0], (uint32_t)res[1]);
   // h turns into this span's histogram of the second digit over its keys in

@@ -205,13 +205,7 @@ __device__ int finish_row(const TopkWs &ws, const int q, const int n, const int 
     if (t < WAVE) {
       const bool have = t < nbound;
       const uint32_t mk = have ? s.ck[s.bidx[t]] : 0u, mp = have ? s.cpos[s.bidx[t]] : 0u;
-      int rank = 0;
-      for (int j = 0; j < nbound; ++j) {
-        const uint32_t ok = s.ck[s.bidx[j]], op = s.cpos[s.bidx[j]];
-        rank += (ok > mk || (ok == mk && op < mp)) ? 1 : 0;
-      }
-      // every lane has read every boundary entry before any is overwritten
-      __builtin_amdgcn_wave_barrier();
+      const int rank = boundary_rank(mk, mp, nbound);
       if (have) s.ck[s.bidx[t]] = rank < r2 ? 0xFFFFFFFFu : 0u;
     }
     lds_barrier();

@@ -50,9 +50,11 @@ __device__ __forceinline__ T block_exclusive_scan(T v, T *sm, T &total) {
 
 // Given an LDS histogram h[NB] and a rank r >= 1 counted from the top, finds
 // the bin B with above(B) < r <= above(B) + h[B] (above(B) = sum of h[b > B]).
-// res[0] = B, res[1] = above(B), visible to all threads on return.
+// res[0] = B, res[1] = above(B), visible to all threads on return.  Returns
+// the histogram's total (the same in every thread), which tells a caller
+// whether the histogram holds what it expects.
 template <int NT, int NB>
-__device__ void find_rank_bin(const uint32_t *h, int r, int *sm, int *res) {
+__device__ int find_rank_bin(const uint32_t *h, int r, int *sm, int *res) {
   constexpr int PER = NB / NT;
   const int hi = NB - PER * (int)threadIdx.x;  // bins [hi - PER, hi), scanned top-down
   int local = 0;
@@ -70,6 +72,7 @@ __device__ void find_rank_bin(const uint32_t *h, int r, int *sm, int *res) {
     acc += c;
   }
   lds_barrier();
+  return total;
 }
 
 template <int NT>
@@ -144,9 +147,9 @@ __device__ __forceinline__ int pack_get(const Packed &p, int rr) {
 // Returns the block total.
 template <int NT>
 __device__ __forceinline__ int ordered_offsets(const Packed &cnt, uint64_t *sm64, int *off) {
-  uint64_t t0, t1;
+  uint64_t t0, t1 = 0, e1 = 0;
   const uint64_t e0 = block_exclusive_scan<NT>(cnt.w0, sm64, t0);
-  const uint64_t e1 = block_exclusive_scan<NT>(cnt.w1, sm64, t1);
+  if constexpr (RowShape<NT>::ROUNDS > PackShape<NT>::PER_WORD) e1 = block_exclusive_scan<NT>(cnt.w1, sm64, t1);
   const Packed ex{e0, e1}, tot{t0, t1};
   int before = 0;
 #pragma unroll
@@ -155,6 +158,20 @@ __device__ __forceinline__ int ordered_offsets(const Packed &cnt, uint64_t *sm64
     before += pack_get<NT>(tot, rr);
   }
   return before;
+}
+
+// Rank of lane l's (key, position) among lanes 0 .. nb - 1 of the
+// wavefront (nb <= WAVE, wave-uniform): how many have a larger key, or the
+// same key at a lower position.  The other lanes' entries are read with
+// v_readlane (a uniform lane index), not through LDS.
+__device__ __forceinline__ int boundary_rank(uint32_t mk, uint32_t mp, int nb) {
+  int rank = 0;
+  for (int j = 0; j < nb; ++j) {
+    const uint32_t ok = (uint32_t)__builtin_amdgcn_readlane((int)mk, j);
+    const uint32_t op = (uint32_t)__builtin_amdgcn_readlane((int)mp, j);
+    rank += (ok > mk || (ok == mk && op < mp)) ? 1 : 0;
+  }
+  return rank;
 }
 
 __device__ __forceinline__ void write_short(int32_t *out, int32_t *count, int q, int n, int k, int nt) {
@@ -187,20 +204,7 @@ __device__ void select_row(const float *row, const int n, const int k, const int
   uint32_t key[RS::PER];
   load_keys<NT>(row, 0, n, key);
   // Digit 1: key[31:21].
-  bool build = hist_src == HIST_BUILD;
-  if (hist_src == HIST_GLOBAL) {
-    int local = 0;
-    for (int b = t; b < TOPK_BINS; b += NT) {
-      const uint32_t v = gh[b];
-      h[b] = v;
-      local += (int)v;
-      gh[b] = 0u;  // each thread clears the bins it read
-    }
-    int tot;
-    block_exclusive_scan<NT>(local, sm, tot);
-    build = tot != n;  // block-uniform
-  }
-  if (build) {
+  auto build = [&] {
     zero_lds<NT>(h, TOPK_BINS);
     lds_barrier();
 #pragma unroll
@@ -208,9 +212,25 @@ __device__ void select_row(const float *row, const int n, const int k, const int
 #pragma unroll
       for (int j = 0; j < TK_J; ++j)
         atomicAdd(&h[key[TK_J * rr + j] >> 21], 1u);  // padding keys land in bin 0
+    lds_barrier();
+  };
+  if (hist_src == HIST_GLOBAL) {
+    for (int b = t; b < TOPK_BINS; b += NT) {
+      h[b] = gh[b];
+      gh[b] = 0u;  // each thread clears the bins it read
+    }
+    lds_barrier();
+  } else if (hist_src == HIST_BUILD) {
+    build();
+  } else {
+    lds_barrier();
   }
-  lds_barrier();
-  find_rank_bin<NT, TOPK_BINS>(h, k, sm, res);
+  // A histogram from memory that does not sum to n (it held more than this
+  // call's counts) is rebuilt from the keys (block-uniform).
+  if (find_rank_bin<NT, TOPK_BINS>(h, k, sm, res) != n && hist_src == HIST_GLOBAL) {
+    build();
+    find_rank_bin<NT, TOPK_BINS>(h, k, sm, res);
+  }
   const uint32_t b1 = (uint32_t)res[0];
   const int r = k - res[1];
   lds_barrier();
@@ -244,16 +264,23 @@ __device__ void select_row(const float *row, const int n, const int k, const int
   const uint32_t kth = (pre << 10) | (uint32_t)res[0];
   const int ties = r2 - res[1];
   // Emit in position order: keys > kth, and the first `ties` keys == kth.
-  Packed tc{0, 0};
-#pragma unroll
-  for (int rr = 0; rr < RS::ROUNDS; ++rr) {
-    int c = 0;
-#pragma unroll
-    for (int j = 0; j < TK_J; ++j) c += (key[TK_J * rr + j] == kth) ? 1 : 0;
-    pack_add<NT>(tc, rr, c);
-  }
+  // Usually every key equal to the k-th is taken (no tie is split), and the
+  // tie ranks, with their block scan, are not needed.
+  const bool all_ties = ties >= (int)h[res[0]];  // block-uniform
   int toff[RS::ROUNDS];
-  ordered_offsets<NT>(tc, sm64, toff);
+#pragma unroll
+  for (int rr = 0; rr < RS::ROUNDS; ++rr) toff[rr] = 0;
+  if (!all_ties) {
+    Packed tc{0, 0};
+#pragma unroll
+    for (int rr = 0; rr < RS::ROUNDS; ++rr) {
+      int c = 0;
+#pragma unroll
+      for (int j = 0; j < TK_J; ++j) c += (key[TK_J * rr + j] == kth) ? 1 : 0;
+      pack_add<NT>(tc, rr, c);
+    }
+    ordered_offsets<NT>(tc, sm64, toff);
+  }
   Packed sc{0, 0};
   uint32_t selbits[RS::ROUNDS];
 #pragma unroll
@@ -264,7 +291,7 @@ __device__ void select_row(const float *row, const int n, const int k, const int
     for (int j = 0; j < TK_J; ++j) {
       const uint32_t kk = key[TK_J * rr + j];
       const bool tie = kk == kth;
-      const bool sel = kk > kth || (tie && tr < ties);
+      const bool sel = kk > kth || (tie && (all_ties || tr < ties));
       tr += tie ? 1 : 0;
       c += sel ? 1 : 0;
       bits |= (uint32_t)sel << j;
