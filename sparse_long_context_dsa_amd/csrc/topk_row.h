@@ -192,7 +192,7 @@ enum HistSource { HIST_BUILD = 0, HIST_GLOBAL = 1, HIST_LDS = 2 };
 // built from the keys instead.  Every thread of the block calls it (it has
 // block barriers, for LDS only).
 template <int NT>
-__device__ void select_row(const float *row, const int n, const int k, const int hist_src, uint32_t *gh,
+__device__ __forceinline__ void select_row(const float *row, const int n, const int k, const int hist_src, uint32_t *gh,
                            uint32_t *h, int *sm, uint64_t *sm64, int *res, int32_t *out, int32_t *count_out) {
   using RS = RowShape<NT>;
   const int t = threadIdx.x;
