@@ -268,8 +268,6 @@ __global__ __launch_bounds__(ST_THREADS) void topk_stream_kernel(SelectArgs a) {
   uint32_t hv[TOPK_BINS / ST_THREADS];
 #pragma unroll
   for (int i = 0; i < TOPK_BINS / ST_THREADS; ++i) hv[i] = gh[t + i * ST_THREADS];
-#pragma unroll
-  for (int i = 0; i < TOPK_BINS / ST_THREADS; ++i) gh[t + i * ST_THREADS] = 0u;  // cleared for the next call
   // Every lane issues the same loads for every round (positions past the
   // wavefront's end read position 0 of the row), so the waits stay exact; a
   // float4 at a position < p1 stays inside the row (ld % 4 == 0).
@@ -454,6 +452,11 @@ __global__ __launch_bounds__(ST_THREADS) void topk_stream_kernel(SelectArgs a) {
   }
   for (int i = tot + t; i < k; i += ST_THREADS) out[i] = -1;  // defensive: tot == k
   if (t == 0 && a.count) a.count[q] = min(tot, k);
+  // The row's first-digit histogram, cleared for the next call.  Stored last:
+  // a store issued before the score loads would hold up every wait on them
+  // (the memory counter counts stores and loads together, in issue order).
+#pragma unroll
+  for (int i = 0; i < TOPK_BINS / ST_THREADS; ++i) gh[t + i * ST_THREADS] = 0u;
 }
 
 __global__ __launch_bounds__(LONG_THREADS) void topk_long_kernel(SelectArgs a) {
@@ -560,15 +563,17 @@ __global__ __launch_bounds__(LONG_THREADS) void topk_finish_kernel(SelectArgs a)
   __shared__ int bidx[WAVE];
   __shared__ int nb_cnt;
   const FinishLds s{ck, cpos, TAIL_CAP, h, off, sm, res, bidx, &nb_cnt};
-  // Every block of the long kernel has read this row's first-digit histogram:
-  // clear it for the next call.
-  for (int b = threadIdx.x; b < TOPK_BINS; b += LONG_THREADS) a.ws.hist[(int64_t)q * TOPK_BINS + b] = 0u;
   int32_t *out = a.idx + (int64_t)q * k;
   const int tot = finish_row<LONG_THREADS>(a.ws, q, n, k, s, [] {}, [&](int o, uint32_t p) {
     if (o < k) out[o] = (int32_t)p;
   });
   for (int i = tot + threadIdx.x; i < k; i += LONG_THREADS) out[i] = -1;  // defensive: tot == k
   if (threadIdx.x == 0 && a.count) a.count[q] = min(tot, k);
+  // Every block of the long kernel has read this row's first-digit histogram:
+  // clear it for the next call.  Stored last, so that no wait on the finish's
+  // own loads waits for these stores (the memory counter counts both, in
+  // issue order).
+  for (int b = threadIdx.x; b < TOPK_BINS; b += LONG_THREADS) a.ws.hist[(int64_t)q * TOPK_BINS + b] = 0u;
 }
 
 hipError_t launch_topk_init(const TopkWs &ws, int num_q, hipStream_t st) {
