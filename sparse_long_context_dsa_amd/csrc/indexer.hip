@@ -277,7 +277,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SEL ? 2 : 3
   if (SEL) {  // the row's scores and first-digit histogram are in LDS
     __shared__ int sm[IDX_WAVES];
     __shared__ uint64_t sm64[IDX_WAVES];
-    __shared__ int res[2];
+    __shared__ int res[TOPK_RES_WORDS];
     __syncthreads();
     select_row<IDX_WAVES * WAVE>(rowbuf, nvis, a.sel_k, HIST_LDS, nullptr, hist, sm, sm64, res,
                                  a.sel_idx + (int64_t)q * a.sel_k, a.sel_count + q);

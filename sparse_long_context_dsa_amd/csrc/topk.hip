@@ -161,7 +161,7 @@ __global__ __launch_bounds__(TK_THREADS) __attribute__((amdgpu_waves_per_eu(3, 3
   __shared__ uint32_t h[TOPK_BINS];
   __shared__ int sm[TK_THREADS / WAVE];
   __shared__ uint64_t sm64[TK_THREADS / WAVE];
-  __shared__ int res[2];
+  __shared__ int res[TOPK_RES_WORDS];
   row_select<TK_THREADS>(a, blockIdx.x, a.q_nvis[blockIdx.x], h, sm, sm64, res);
 }
 
@@ -172,7 +172,7 @@ __global__ __launch_bounds__(LONG_THREADS) void topk_row_wide_kernel(SelectArgs 
   __shared__ uint32_t h[TOPK_BINS];
   __shared__ int sm[LONG_THREADS / WAVE];
   __shared__ uint64_t sm64[LONG_THREADS / WAVE];
-  __shared__ int res[2];
+  __shared__ int res[TOPK_RES_WORDS];
   row_select<LONG_THREADS>(a, blockIdx.x, a.q_nvis[blockIdx.x], h, sm, sm64, res);
 }
 
@@ -242,7 +242,7 @@ __global__ __launch_bounds__(ST_THREADS) void topk_stream_kernel(SelectArgs a) {
   __shared__ uint32_t h[TOPK_BINS];
   __shared__ int sm[ST_WAVES];
   __shared__ uint64_t sm64[ST_WAVES];
-  __shared__ int res[2];
+  __shared__ int res[TOPK_RES_WORDS];
   __shared__ uint32_t ck[ST_CAP];    // candidate keys
   __shared__ uint32_t cpos[ST_CAP];  // candidate positions
   __shared__ uint32_t bm[ST_WORDS];  // selected positions
@@ -468,7 +468,7 @@ __global__ __launch_bounds__(LONG_THREADS) void topk_long_kernel(SelectArgs a) {
   __shared__ uint32_t h[TOPK_BINS];
   __shared__ int sm[LONG_THREADS / WAVE];
   __shared__ uint64_t sm64[LONG_THREADS / WAVE];
-  __shared__ int res[2];
+  __shared__ int res[TOPK_RES_WORDS];
   if (n <= TOPK_ROW_MAX) {  // a short row of a batch with long rows: its first block selects it
     if (c == 0) row_select<LONG_THREADS>(a, q, n, h, sm, sm64, res);
     return;
@@ -557,7 +557,7 @@ __global__ __launch_bounds__(LONG_THREADS) void topk_finish_kernel(SelectArgs a)
   if (n <= TOPK_ROW_MAX) return;  // selected whole by topk_long_kernel
   __shared__ uint32_t h[TOPK_BINS];
   __shared__ int sm[LONG_THREADS / WAVE];
-  __shared__ int res[2];
+  __shared__ int res[TOPK_RES_WORDS];
   __shared__ uint32_t ck[TAIL_CAP], cpos[TAIL_CAP];
   __shared__ int off[TOPK_MAX_LISTS + 1];
   __shared__ int bidx[WAVE];

@@ -48,9 +48,14 @@ __device__ __forceinline__ T block_exclusive_scan(T v, T *sm, T &total) {
   return before + inc - v;
 }
 
+// Words of the block's small result slot `res` (find_rank_bin's answer and
+// the boundary-key counter of select_row).
+constexpr int TOPK_RES_WORDS = 4;
+
 // Given an LDS histogram h[NB] and a rank r >= 1 counted from the top, finds
 // the bin B with above(B) < r <= above(B) + h[B] (above(B) = sum of h[b > B]).
-// res[0] = B, res[1] = above(B), visible to all threads on return.  Returns
+// res[0] = B, res[1] = above(B), res[2] = h[B], visible to all threads on
+// return (so that h may be reused at once).  Returns
 // the histogram's total (the same in every thread), which tells a caller
 // whether the histogram holds what it expects.
 template <int NT, int NB>
@@ -68,6 +73,7 @@ __device__ int find_rank_bin(const uint32_t *h, int r, int *sm, int *res) {
     if (acc < r && acc + c >= r) {
       res[0] = hi - i;
       res[1] = acc;
+      res[2] = c;
     }
     acc += c;
   }
@@ -203,6 +209,7 @@ __device__ __forceinline__ void select_row(const float *row, const int n, const 
   }
   uint32_t key[RS::PER];
   load_keys<NT>(row, 0, n, key);
+  if (t == 0) res[3] = 0;  // boundary keys collected (below)
   // Digit 1: key[31:21].
   auto build = [&] {
     zero_lds<NT>(h, TOPK_BINS);
@@ -248,25 +255,64 @@ __device__ __forceinline__ void select_row(const float *row, const int n, const 
   find_rank_bin<NT, TOPK_BINS>(h, r, sm, res);
   const uint32_t pre = (b1 << 11) | (uint32_t)res[0];
   const int r2 = r - res[1];
-  lds_barrier();
-  // Digit 3: key[9:0] of the keys with key[31:10] == pre.
-  zero_lds<NT>(h, 1024);
-  lds_barrier();
+  const int nbound = res[2];  // keys with key[31:10] == pre
+  uint32_t kth;
+  int ties, tie_total;
+  if (nbound <= WAVE) {  // block-uniform
+    // Few keys share the boundary prefix (the usual case): they are gathered
+    // into h (free: find_rank_bin has left its answer in res) and one
+    // wavefront ranks them by (key descending, position ascending); the
+    // r2-th is the k-th key.  No third digit.
 #pragma unroll
-  for (int rr = 0; rr < RS::ROUNDS; ++rr)
+    for (int rr = 0; rr < RS::ROUNDS; ++rr)
 #pragma unroll
-    for (int j = 0; j < TK_J; ++j) {
-      const uint32_t kk = key[TK_J * rr + j];
-      if ((kk >> 10) == pre) atomicAdd(&h[kk & 1023u], 1u);
+      for (int j = 0; j < TK_J; ++j)
+        if ((key[TK_J * rr + j] >> 10) == pre) {
+          const int sl = atomicAdd(&res[3], 1);
+          h[sl] = key[TK_J * rr + j];
+          h[WAVE + sl] = (uint32_t)slot_pos<NT>(t, rr, j);
+        }
+    lds_barrier();
+    if (t < WAVE) {
+      const bool have = t < nbound;
+      const uint32_t mk = have ? h[t] : 0u, mp = have ? h[WAVE + t] : 0u;
+      const int rank = boundary_rank(mk, mp, nbound);
+      const uint64_t at = __ballot(have && rank == r2 - 1);
+      const uint32_t kv = (uint32_t)__builtin_amdgcn_readlane((int)mk, (int)__builtin_ctzll(at));
+      const int gt = (int)__popcll(__ballot(have && mk > kv));
+      const int eq = (int)__popcll(__ballot(have && mk == kv));
+      if (t == 0) {
+        res[0] = (int)kv;
+        res[1] = gt;
+        res[2] = eq;
+      }
     }
-  lds_barrier();
-  find_rank_bin<NT, 1024>(h, r2, sm, res);
-  const uint32_t kth = (pre << 10) | (uint32_t)res[0];
-  const int ties = r2 - res[1];
+    lds_barrier();
+    kth = (uint32_t)res[0];
+    ties = r2 - res[1];
+    tie_total = res[2];
+  } else {
+    lds_barrier();
+    // Digit 3: key[9:0] of the keys with key[31:10] == pre.
+    zero_lds<NT>(h, 1024);
+    lds_barrier();
+#pragma unroll
+    for (int rr = 0; rr < RS::ROUNDS; ++rr)
+#pragma unroll
+      for (int j = 0; j < TK_J; ++j) {
+        const uint32_t kk = key[TK_J * rr + j];
+        if ((kk >> 10) == pre) atomicAdd(&h[kk & 1023u], 1u);
+      }
+    lds_barrier();
+    find_rank_bin<NT, 1024>(h, r2, sm, res);
+    kth = (pre << 10) | (uint32_t)res[0];
+    ties = r2 - res[1];
+    tie_total = res[2];
+  }
   // Emit in position order: keys > kth, and the first `ties` keys == kth.
   // Usually every key equal to the k-th is taken (no tie is split), and the
   // tie ranks, with their block scan, are not needed.
-  const bool all_ties = ties >= (int)h[res[0]];  // block-uniform
+  const bool all_ties = ties >= tie_total;  // block-uniform
   int toff[RS::ROUNDS];
 #pragma unroll
   for (int rr = 0; rr < RS::ROUNDS; ++rr) toff[rr] = 0;
