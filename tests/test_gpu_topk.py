@@ -207,3 +207,27 @@ def test_short_rows_both_row_kernels(nq):
     nvis[0], rows[0] = 16384, rng.standard_normal(16384).astype(np.float32)
     assert_same(rows, nvis, 2048, f"short rows, {nq}")
     assert_same(rows, nvis, 5, f"short rows, {nq}, k = 5")
+
+
+def _split_tie_row(rng, n, k, m):
+    """N(0,1) scores with m more copies of the k-th largest value placed at
+    random lower-ranked positions: k - 1 keys are larger and m + 1 equal it,
+    so one of the ties is taken (the lowest position) and the boundary holds
+    few keys (the one-wavefront ranking, not the third digit)."""
+    v = rng.standard_normal(n).astype(np.float32)
+    order = np.argsort(-v, kind="stable")
+    kth = v[order[k - 1]]
+    below = order[k:k + 2000]
+    v[rng.choice(below, min(m, len(below)), replace=False)] = kth
+    return v
+
+
+@pytest.mark.parametrize("shape", ["stream", "row_wide", "row", "long"])
+def test_few_ties_split_at_the_threshold(shape):
+    banner(f"topk split ties, {shape}")
+    rng = np.random.default_rng(2024 + len(shape))
+    k = 2048
+    nvis = {"stream": [4096, 16384, 50000, 131072], "row_wide": [4096, 16384, 2100],
+            "row": [3000] * 260, "long": [131072, 70000] * 20}[shape]
+    rows = [_split_tie_row(rng, n, k, int(rng.integers(1, 12))) for n in nvis]
+    assert_same(rows, nvis, k, f"split ties {shape}")
