@@ -141,13 +141,17 @@ __global__ __launch_bounds__(MLA_THREADS, 1) void mla_hg_kernel(MlaHgArgs p) {
   constexpr int Q_PARTS = 32 * ROW_BYTES / 1024 / MLA_WAVES;  // 9 KiB-loads per wavefront
   static_assert(Q_PARTS * 1024 * MLA_WAVES == 32 * ROW_BYTES && 32 * ROW_BYTES <= sizeof(tb1), "q stage fits");
   uint4 qb[2][18];
+  // The buffer form, as for the gathers: the compiler counts these loads
+  // exactly, so waits on the position loads issued before them need not wait
+  // for them (the global form made that wait drain every load in flight).
   auto load_q = [&]() {
-    const uint8_t *qg = reinterpret_cast<const uint8_t *>(a.q + ((int64_t)q * 128 + 32 * hg) * 576);
+    const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(a.q + ((int64_t)q * 128 + 32 * hg) * 576), (short)0, 0xFFFFFFFF, 0x00020000);
 #pragma unroll
     for (int j = 0; j < Q_PARTS; ++j) {
       const int part = wave * Q_PARTS + j;
-      __builtin_amdgcn_global_load_lds(qg + 1024 * part + 16 * lane, (lds_void *)(&tb1[0][0] + 1024 * part), 16, 0,
-                                       0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (lds_void *)(&tb1[0][0] + 1024 * part), 16,
+                                               1024 * part + 16 * lane, 0, 0, 0);
     }
   };
 
