@@ -49,6 +49,8 @@ namespace dsa {
 constexpr int LONG_THREADS = TOPK_LONG_WAVES * WAVE;
 constexpr int LONG_ROUNDS = TOPK_WAVE_SPAN / 512;  // rounds of 512 positions per wavefront
 constexpr int TAIL_CAP = 12288;                     // candidates the finishing block keeps in LDS
+constexpr int FINISH_THREADS = 1024;                // threads of the finishing block (512: top-k stage
+                                                    // 0.5 us slower at 64 x 131072; 256: 4 us slower)
 constexpr int TOPK_ROW_WIDE_MAX_Q = 256;            // up to one row per CU: 1024-thread row blocks
 static_assert(TOPK_CHUNK == TOPK_ROW_MAX, "one histogram block covers one chunk");
 
@@ -550,13 +552,13 @@ __global__ __launch_bounds__(LONG_THREADS) void topk_long_kernel(SelectArgs a) {
   for (int i = 0; i < TOPK_BINS / LONG_THREADS; ++i) h2[t + i * LONG_THREADS] = h[t + i * LONG_THREADS];
 }
 
-__global__ __launch_bounds__(LONG_THREADS) void topk_finish_kernel(SelectArgs a) {
+__global__ __launch_bounds__(FINISH_THREADS) void topk_finish_kernel(SelectArgs a) {
   const int q = blockIdx.x;
   const int n = a.q_nvis[q];
   const int k = a.k;
   if (n <= TOPK_ROW_MAX) return;  // selected whole by topk_long_kernel
   __shared__ uint32_t h[TOPK_BINS];
-  __shared__ int sm[LONG_THREADS / WAVE];
+  __shared__ int sm[FINISH_THREADS / WAVE];
   __shared__ int res[TOPK_RES_WORDS];
   __shared__ uint32_t ck[TAIL_CAP], cpos[TAIL_CAP];
   __shared__ int off[TOPK_MAX_LISTS + 1];
@@ -564,16 +566,16 @@ __global__ __launch_bounds__(LONG_THREADS) void topk_finish_kernel(SelectArgs a)
   __shared__ int nb_cnt;
   const FinishLds s{ck, cpos, TAIL_CAP, h, off, sm, res, bidx, &nb_cnt};
   int32_t *out = a.idx + (int64_t)q * k;
-  const int tot = finish_row<LONG_THREADS>(a.ws, q, n, k, s, [] {}, [&](int o, uint32_t p) {
+  const int tot = finish_row<FINISH_THREADS>(a.ws, q, n, k, s, [] {}, [&](int o, uint32_t p) {
     if (o < k) out[o] = (int32_t)p;
   });
-  for (int i = tot + threadIdx.x; i < k; i += LONG_THREADS) out[i] = -1;  // defensive: tot == k
+  for (int i = tot + threadIdx.x; i < k; i += FINISH_THREADS) out[i] = -1;  // defensive: tot == k
   if (threadIdx.x == 0 && a.count) a.count[q] = min(tot, k);
   // Every block of the long kernel has read this row's first-digit histogram:
   // clear it for the next call.  Stored last, so that no wait on the finish's
   // own loads waits for these stores (the memory counter counts both, in
   // issue order).
-  for (int b = threadIdx.x; b < TOPK_BINS; b += LONG_THREADS) a.ws.hist[(int64_t)q * TOPK_BINS + b] = 0u;
+  for (int b = threadIdx.x; b < TOPK_BINS; b += FINISH_THREADS) a.ws.hist[(int64_t)q * TOPK_BINS + b] = 0u;
 }
 
 hipError_t launch_topk_init(const TopkWs &ws, int num_q, hipStream_t st) {
@@ -614,7 +616,7 @@ hipError_t launch_topk_select(const float *scores, int64_t ld, const int32_t *q_
   hipLaunchKernelGGL(topk_long_kernel, dim3((unsigned)blocks), dim3(LONG_THREADS), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_finish_kernel, dim3((unsigned)num_q), dim3(LONG_THREADS), 0, st, a);
+  hipLaunchKernelGGL(topk_finish_kernel, dim3((unsigned)num_q), dim3(FINISH_THREADS), 0, st, a);
   return hipGetLastError();
 }
 

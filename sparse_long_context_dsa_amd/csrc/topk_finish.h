@@ -41,7 +41,8 @@ __device__ int finish_row(const TopkWs &ws, const int q, const int n, const int 
   constexpr int BPT = TOPK_BINS / NT;                   // histogram bins per thread
   constexpr int NW = NT / WAVE;
   constexpr int LB = 16;                                // lists per wavefront per load batch
-  constexpr int LB0 = 4;   // lists per wavefront requested with the counts (NW * LB0 cover 2^17 positions at NW = 16)
+  constexpr int LB0 = (4 * TOPK_LONG_WAVES + NW - 1) / NW;  // lists per wavefront requested with the counts:
+                                                              // NW * LB0 lists cover 2^17 positions
   constexpr int E0 = 2;    // their entries per lane requested then: a 2048-position list rarely holds more than 128
   const int t = threadIdx.x;
   const int lane = t & (WAVE - 1), wave = t / WAVE;
