@@ -47,10 +47,10 @@ CALIB_BYTES = 1 << 30           # size of the calibration copy (read and written
 # same counter reads for the 1 GiB calibration copy.  Valid only for the kernel
 # source it was measured on: the figure is dropped when indexer.hip changes.
 INDEXER_TRAFFIC = {
-    "source_sha": "7451e2af1996054c",
-    "fetch_kib": 543033, "write_kib": 35887,          # raw counter readings
+    "source_sha": "c6c67e20879b8327",
+    "fetch_kib": 543112, "write_kib": 35887,          # raw counter readings
     "calib_fetch_kib": 524295, "calib_write_kib": 1048576,  # the 1 GiB copy
-    "bytes_per_launch": (543033 * 2 + 35887) * 1024,
+    "bytes_per_launch": (543112 * 2 + 35887) * 1024,
 }
 
 

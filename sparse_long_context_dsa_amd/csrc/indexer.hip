@@ -112,6 +112,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SEL ? 2 : 3
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int seq = a.q_seq[q];
 
+  // Physical row of each 64-key step of this wavefront's run (a step never
+  // straddles a cache block), one step per lane, looked up once: the loop then
+  // issues its key loads without waiting on a block-table read.  Every lane
+  // looks one up (positions clamped into the history), so no branch merges
+  // its value with a constant, which would make the compiler wait for all
+  // loads in flight there.
+  const int s_begin = (chunk * IDX_WAVES + wave) * kpw;
+  const int s_end = min(s_begin + kpw, nvis);
+  const int64_t lane_row = phys_row(a.map, seq, max(0, min(s_begin + 64 * lane, nvis - 1)));
+  // The first step's keys are requested before q and the weights are staged,
+  // so that their round trip overlaps the staging's instead of following it.
+  const int nsteps = s_begin < s_end ? (s_end - s_begin + 63) >> 6 : 0;
+  KeyStep kb0, kb1;
+  if (nsteps > 0) load_step<E8M0>(a, readlane64(lane_row, 0), s_begin, nvis, lane, kb0);
+
   __shared__ uint32_t hist[(HIST || SEL) ? TOPK_BINS : 1];
   // Per-wavefront staging of 256 scores: written as 16-byte stores (1 KiB per
   // wavefront instruction), which the memory system takes much better than
@@ -123,19 +138,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SEL ? 2 : 3
   // and shared by the four wavefronts through LDS (each wavefront reading it
   // from memory in the operand layout took 4x the requests, 16 rows apart).
   __shared__ __attribute__((aligned(16))) uint8_t qlds[SEL ? 16 : 64 * 128];
-  if (!SEL) {
-    static_assert(64 * 128 == 2 * 16 * IDX_WAVES * WAVE, "two 16-byte pieces per thread");
-    const uint4 *qsrc = reinterpret_cast<const uint4 *>(a.q8 + (int64_t)q * (64 * 128));
-    uint4 *qdst = reinterpret_cast<uint4 *>(qlds);
-    qdst[threadIdx.x] = qsrc[threadIdx.x];
-    qdst[threadIdx.x + IDX_WAVES * WAVE] = qsrc[threadIdx.x + IDX_WAVES * WAVE];
-  }
   // The 64 epilogue weights w * q_scale, likewise once per block.
   __shared__ __attribute__((aligned(16))) float wq[64];
-  if (threadIdx.x < 64) {
-    const float qs = a.q_scale ? a.q_scale[(int64_t)q * 64 + threadIdx.x] : 1.0f;
-    wq[threadIdx.x] = a.w[(int64_t)q * 64 + threadIdx.x] * qs;
+  // All of the staging's loads go out before any of their values is used:
+  // every thread loads (weight and scale of head t % 64, from a valid array
+  // when there are no q scales), and only the stores depend on the thread.
+  static_assert(64 * 128 == 2 * 16 * IDX_WAVES * WAVE, "two 16-byte pieces per thread");
+  const uint4 *qsrc = reinterpret_cast<const uint4 *>(a.q8 + (int64_t)q * (64 * 128));
+  uint4 qv0, qv1;
+  if (!SEL) {
+    qv0 = qsrc[threadIdx.x];
+    qv1 = qsrc[threadIdx.x + IDX_WAVES * WAVE];
   }
+  const int hw = (int)(threadIdx.x & 63);
+  const float wv = a.w[(int64_t)q * 64 + hw];
+  const float qsv = (a.q_scale ? a.q_scale : a.w)[(int64_t)q * 64 + hw];
+  __builtin_amdgcn_sched_barrier(0);  // the stores below wait; the loads stay above them
+  if (!SEL) {
+    uint4 *qdst = reinterpret_cast<uint4 *>(qlds);
+    qdst[threadIdx.x] = qv0;
+    qdst[threadIdx.x + IDX_WAVES * WAVE] = qv1;
+  }
+  if (threadIdx.x < 64) wq[threadIdx.x] = wv * (a.q_scale ? qsv : 1.0f);
   if (HIST || SEL) {
     for (int b = threadIdx.x; b < TOPK_BINS; b += blockDim.x) hist[b] = 0u;
   }
@@ -169,15 +193,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SEL ? 2 : 3
     coef[mt][3] = c4.w;
   }
 
-  const int s_begin = (chunk * IDX_WAVES + wave) * kpw;
-  const int s_end = min(s_begin + kpw, nvis);
   float *srow = a.scores + (int64_t)q * a.ld;
-
-  // Physical row of each 64-key step of this wavefront's run (a step never
-  // straddles a cache block), one step per lane, looked up once: the loop then
-  // issues its key loads without waiting on a block-table read.
-  int64_t lane_row = 0;
-  if (s_begin + 64 * lane < s_end) lane_row = phys_row(a.map, seq, s_begin + 64 * lane);
 
   // A finished group of 256 scores is stored one step late, after the next
   // step's key loads are issued, so that the wait for those loads (vector
@@ -258,9 +274,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(SEL ? 2 : 3
 
   // Steps are taken in pairs while both have a successor to prefetch; the
   // last one or two are peeled, so the prefetch in the loop is unconditional.
-  const int nsteps = s_begin < s_end ? (s_end - s_begin + 63) >> 6 : 0;
-  KeyStep kb0, kb1;
-  if (nsteps > 0) load_step<E8M0>(a, readlane64(lane_row, 0), s_begin, nvis, lane, kb0);
   int i = 0;
   for (; i + 2 < nsteps; i += 2) {
     step(s_begin + 64 * i, kb0, &kb1);
