@@ -121,6 +121,23 @@ def test_long_rows_mixed_lengths(paged):
     check_queries(wl, g, out, lse, idx, [0, 2, 3, 4, 6, 8, 9])
 
 
+@pytest.mark.parametrize("lens", [[9000, 12000, 5000], [40000] * 16, [131072] * 8 + [20000] * 56],
+                         ids=["row-blocks", "streaming", "two-kernel"])
+def test_rows_of_mostly_negative_scores(lens):
+    """Rows whose head weights are all negative score below zero almost
+    everywhere (the k-th key among negative keys, the threshold bins in the
+    lower half of the first digit), beside rows with weights of either sign:
+    on every top-k path the forward must select what the standalone top-k
+    selects."""
+    banner(f"forward, negative scores, {len(lens)} rows up to {max(lens)}")
+    wl = make_custom(seq_lens=lens, device="cuda", seed=61)
+    wl.w[::2] = -wl.w[::2].abs()   # every other query: all weights negative
+    g = GpuInputs(wl)
+    out, lse, idx = run_forward(g)
+    assert torch.equal(idx, _standalone_topk(g, wl.k)), "forward selection differs from the standalone top-k"
+    check_queries(wl, g, out, lse, idx, [0, 1])
+
+
 @pytest.mark.parametrize("k", [2048, 100])
 def test_long_rows_heavy_ties(k):
     """Five distinct key rows repeated along the cache: each score takes one of
